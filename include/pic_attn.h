@@ -1,0 +1,220 @@
+/*
+ * pic_attn.h -- C ABI of the MI355X (gfx950) library for position-independent
+ * attention over reused KV spans, with query-centric selection and cache
+ * fusion.
+ *
+ * Sources of the operations (gist.science pages):
+ *   [MiniPIC]  "MiniPIC: flexible position-independent caching in <100 LOC"
+ *              (2606.13126), section 2.1 "Implementacion de KV Libre de
+ *              Posicion": keys are stored unrotated, RoPE is applied inside the
+ *              attention kernel at per-request logical positions,
+ *              score(t, j) = (R_t q_t)^T (R_pi(j) k~_j) / sqrt(d), and one
+ *              physical block serves concurrent requests at different offsets
+ *              without being duplicated, re-rotated or mutated.
+ *   [QCFuse]   "QCFuse: Query-Centric Cache Fusion for Efficient RAG
+ *              Inference" (2604.08585), methodology B (critical-layer attention
+ *              profiling: the query's attention over one layer's K cache picks
+ *              the top context tokens whose indices guide recomputation) and
+ *              C / phase 4 (the recomputed tokens are mixed back into the
+ *              stored cache).
+ *
+ * Conventions shared by every entry point
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Pointers documented as "device" must point to device memory of the
+ *     context's GPU; "host" pointers to host memory.  The caller owns all
+ *     memory; the library never frees or retains caller pointers after a call
+ *     returns, and allocates only in pic_ctx_create.
+ *   - Every op is asynchronous on the given stream (a hipStream_t passed as
+ *     void*, NULL = the default stream).  Results are valid once the stream has
+ *     reached the op.  Host-detectable argument errors return before anything
+ *     is launched and leave all memory untouched.
+ *   - Logical positions: 0 <= pi < max_position.  pi = -1 marks an empty or
+ *     masked slot.  Key j is visible to a query at position t iff
+ *     0 <= pi(j) <= t (positional causality).  Device-side values outside
+ *     these ranges (a block id >= num_blocks, pi >= max_position, q_pos
+ *     outside [0, max_position)) never cause an out-of-bounds access: such a
+ *     key is treated as masked and such a query as seeing nothing.
+ *   - Grouped-query attention: q head h reads kv head h / (Hq / Hkv).
+ *   - A context may be used by one host thread at a time.
+ */
+#ifndef PIC_ATTN_H
+#define PIC_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PIC_BLOCK_SIZE 16
+
+typedef enum {
+    PIC_OK = 0,
+    PIC_ERR_INVALID_ARG = 1,   /* null pointer, inconsistent sizes, bad range */
+    PIC_ERR_UNSUPPORTED = 2,   /* head_dim not 64/128, block_size not 16, ... */
+    PIC_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    PIC_ERR_HIP = 4            /* a HIP runtime call failed; see last_error */
+} pic_status;
+
+typedef enum {
+    PIC_OP_PREFILL = 0,
+    PIC_OP_DECODE = 1,
+    PIC_OP_SELECT = 2
+} pic_op;
+
+/* Model geometry and RoPE parameters.  RoPE pairs element i with i + d/2 and
+ * turns the pair by the angle pos * rope_theta^(-2i/d), counter-clockwise
+ * (x_i' = x_i cos - x_{i+d/2} sin, x_{i+d/2}' = x_i sin + x_{i+d/2} cos). */
+typedef struct {
+    int32_t num_q_heads;    /* Hq, a multiple of num_kv_heads */
+    int32_t num_kv_heads;   /* Hkv */
+    int32_t head_dim;       /* d: 64 or 128 */
+    int32_t block_size;     /* must be PIC_BLOCK_SIZE */
+    int32_t max_position;   /* rows of the cos/sin table, 1 .. 1<<22 */
+    double rope_theta;      /* > 0 */
+} pic_config;
+
+typedef struct pic_ctx pic_ctx;
+
+/* The paged pool of cached K and V ([MiniPIC] section 2.1: unrotated keys;
+ * blocks shared across requests).  Device memory.
+ *   k: [num_blocks][Hkv][16][d]  unrotated keys, token-major within a block
+ *   v: [num_blocks][Hkv][d][16]  values, head-dim-major within a block (so
+ *      the 16 tokens of one channel are contiguous)
+ * Only kv_fuse_scatter writes the pool, and only the request-private blocks
+ * appended for fused rows. */
+typedef struct {
+    uint16_t *k;
+    uint16_t *v;
+    int32_t num_blocks;
+} pic_kv_pool;
+
+/* Per-request view of the pool.  Slot j (0 <= j < kv_len[r]) of request r is
+ * token (j % 16) of physical block block_table[r][j / 16]; kv_pos[r][j] is its
+ * logical position pi_r(j) in this request ([MiniPIC] section 2.1).
+ *   block_table: device int32 [batch][max_blocks]
+ *   kv_len:      device int32 [batch], 0 <= kv_len[r] <= max_kv_len
+ *   kv_pos:      device int32 [batch][max_blocks * 16]
+ *   max_kv_len:  host-side upper bound of kv_len (sizes the launch)
+ * The ops other than kv_fuse_scatter only read these arrays. */
+typedef struct {
+    int32_t batch;
+    int32_t max_blocks;
+    int32_t max_kv_len;
+    int32_t *block_table;
+    int32_t *kv_len;
+    int32_t *kv_pos;
+} pic_req_table;
+
+/* Query tokens of a prefill-style call (several per request).
+ *   q:       device bf16 [total_q][Hq][d], unrotated (rotated in-kernel at q_pos)
+ *   q_start: device int32 [batch + 1], CSR of each request's query rows
+ *   q_pos:   device int32 [total_q], logical position of each query token
+ *   max_q_len: host-side upper bound of q_start[r+1] - q_start[r] */
+typedef struct {
+    const uint16_t *q;
+    const int32_t *q_start;
+    const int32_t *q_pos;
+    int32_t total_q;
+    int32_t max_q_len;
+} pic_queries;
+
+/* Spans to select from ([QCFuse] methodology B, read per span).
+ *   span_req, span_start, span_len: device int32 [n_spans]; span s covers
+ *     request-sequence slots [span_start, span_start + span_len) of request
+ *     span_req.  Spans of a request must be listed together, requests in
+ *     ascending order.
+ *   sel_off: device int32 [n_spans + 1], CSR of the output: span s gets
+ *     k_s = sel_off[s+1] - sel_off[s] indices (pic_select_offsets computes
+ *     them from a ratio). */
+typedef struct {
+    int32_t n_spans;
+    const int32_t *span_req;
+    const int32_t *span_start;
+    const int32_t *span_len;
+    const int32_t *sel_off;
+} pic_spans;
+
+/* Create a context on the current HIP device: validates the config and builds
+ * the RoPE cos/sin table (computed in double on the host, stored as fp32 on
+ * the device: 2 * max_position * d/2 * 4 bytes).  *out is NULL on failure. */
+pic_status pic_ctx_create(const pic_config *cfg, pic_ctx **out);
+void pic_ctx_destroy(pic_ctx *ctx);
+const char *pic_status_str(pic_status s);
+/* Text of the last error recorded on ctx ("" if none). */
+const char *pic_ctx_last_error(const pic_ctx *ctx);
+
+/* Bytes of device workspace that `op` needs for these sizes (0 is possible).
+ * For PIC_OP_DECODE total_q and max_q_len are ignored (one query per request).
+ * For PIC_OP_SELECT the figure covers the case lse == NULL and mass == NULL. */
+pic_status pic_workspace_bytes(const pic_ctx *ctx, pic_op op, const pic_req_table *req,
+                               int32_t total_q, int32_t max_q_len, size_t *bytes);
+
+/* Selection budget per span ([QCFuse] methodology B, top fraction per span):
+ * k_s = floor(ratio * span_len[s] + 0.5), written as a CSR (sel_off[0] = 0,
+ * sel_off[s+1] = sel_off[s] + k_s).  Host arrays; pure host function. */
+pic_status pic_select_offsets(int32_t n_spans, const int32_t *span_len_host, double ratio,
+                              int32_t *sel_off_host);
+
+/* Attention of each request's query tokens over its cached keys
+ * ([MiniPIC] section 2.1 score equation), softmax over the visible keys.
+ *   out: device bf16 [total_q][Hq][d]
+ *   lse: device fp32 [total_q][Hq] natural-log log-sum-exp of the scaled
+ *        scores, or NULL.  A row with no visible key gets out = 0,
+ *        lse = -inf.
+ *   ws:  device workspace of at least pic_workspace_bytes(PIC_OP_PREFILL). */
+pic_status pic_attn_prefill(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_table *req,
+                            const pic_queries *qs, uint16_t *out, float *lse, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* One query token per request (generation step), same definition.
+ *   q:     device bf16 [batch][Hq][d], unrotated
+ *   q_pos: device int32 [batch]
+ *   out:   device bf16 [batch][Hq][d];  lse: device fp32 [batch][Hq] or NULL */
+pic_status pic_attn_decode(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_table *req,
+                           const uint16_t *q, const int32_t *q_pos, uint16_t *out, float *lse,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Query-centric selection ([QCFuse] methodology B; phase 3 of the German
+ * page): reads only K.  mass_r[j] = sum over request r's query rows (t, h) of
+ * softmax probability p_{t,h}(j) = exp(s_{t,h,j} - lse_{t,h}) for visible j;
+ * then per span the k_s slots of largest mass (ties to the lower slot index),
+ * among slots with pi >= 0, written to sel_idx[sel_off[s] ..] in ascending
+ * order.  If a span has fewer candidates than k_s, the remaining entries are
+ * -1.
+ *   lse:     device fp32 [total_q][Hq] from pic_attn_prefill over the same
+ *            cache and queries, or NULL (then computed here).
+ *   sel_idx: device int32 [sel_off[n_spans]]
+ *   mass:    device fp32 [batch][max_blocks * 16] or NULL; entries
+ *            j < kv_len[r] are written (0 for masked slots).
+ *   max_sel: host-side value of sel_off[n_spans] (bounds sel_idx). */
+pic_status qc_score_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_table *req,
+                           const pic_queries *qs, const float *lse, const pic_spans *spans,
+                           int32_t max_sel, int32_t *sel_idx, float *mass, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* Cache fusion ([QCFuse] "Lo esencial" step 4 and phase 4: recomputed tokens
+ * mixed into the stored cache) without writing shared blocks ([MiniPIC]
+ * section 2.1).  For request r, its selected slots are
+ * sel_idx[sel_req_off[r] .. sel_req_off[r+1]) (distinct, each < kv_len[r], or
+ * -1) and row i of k_new / v_new ([n_sel][Hkv][d], bf16, unrotated K) is the
+ * recomputed token of entry i.  With base = 16 * ceil(kv_len[r] / 16):
+ *   slots kv_len[r] .. base-1 get pi = -1;
+ *   slot base + i receives row i bit for bit (K and V) and pi of the selected
+ *   slot, whose pi becomes -1 (an entry of -1 leaves slot base + i empty);
+ *   kv_len[r] becomes base + count.
+ * Precondition: block_table[r][base/16 ..] already names request-private
+ * blocks with room for the rows; a block id outside [0, num_blocks) is
+ * skipped.  n_sel = sel_req_off[batch] (host value).  max_rows_per_req is a
+ * host bound of sel_req_off[r+1] - sel_req_off[r]. */
+pic_status kv_fuse_scatter(pic_ctx *ctx, pic_kv_pool *pool, pic_req_table *req,
+                           const int32_t *sel_idx, const int32_t *sel_req_off,
+                           const uint16_t *k_new, const uint16_t *v_new, int32_t n_sel,
+                           int32_t max_rows_per_req, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PIC_ATTN_H */

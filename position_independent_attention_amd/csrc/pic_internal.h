@@ -1,0 +1,125 @@
+// Internal declarations of the gfx950 library: launch parameter blocks and the
+// host-side launchers implemented in the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pic {
+
+constexpr int kBlock = 16;        // tokens per pool block
+constexpr int kTileN = 64;        // keys per staged tile in the prefill-style kernels
+constexpr int kThreads = 256;     // 4 wave64 per workgroup
+constexpr int kWaves = 4;
+constexpr int kDecodeSplit = 1024;  // keys per decode workgroup (multiple of 128)
+
+enum Mode : int { kAttn = 0, kLse = 1, kMass = 2 };
+
+// Everything one prefill-style launch needs.  Pointers are device pointers.
+struct FwdParams {
+    const uint16_t *k_pool;
+    const uint16_t *v_pool;
+    int32_t num_blocks;
+    const int32_t *block_table;
+    const int32_t *kv_len;
+    const int32_t *kv_pos;
+    int32_t max_blocks;
+    const uint16_t *q;
+    const int32_t *q_start;   // [B+1]
+    const int32_t *q_pos;     // [total_q]
+    int32_t batch, total_q;
+    int32_t hq, hkv, group;
+    const float *cos_tab;     // [max_pos][d/2]
+    const float *sin_tab;
+    int32_t max_pos;
+    float scale_log2;         // log2(e) / sqrt(d)
+    int32_t max_kv_len;       // host bound on kv_len (clamps every key range)
+    int32_t split_len;        // keys per split, multiple of kTileN
+    int32_t num_splits;
+    int32_t row_blocks;       // workgroups along the packed (token, head) rows
+    // outputs
+    uint16_t *out;            // [total_q][hq][d] bf16 (num_splits == 1)
+    float *lse;               // [total_q][hq] natural log, nullable
+    float *part_o;            // [num_splits][total_q][hq][d]
+    float *part_ml;           // [num_splits][total_q][hq][2] (max in log2 units, sum)
+    // selection mass
+    const float *lse_in;      // [total_q][hq] natural log
+    float *mass_part;         // [B][hkv][row_blocks][mass_stride]
+    int32_t mass_stride;
+};
+
+struct DecodeParams {
+    const uint16_t *k_pool;
+    const uint16_t *v_pool;
+    int32_t num_blocks;
+    const int32_t *block_table;
+    const int32_t *kv_len;
+    const int32_t *kv_pos;
+    int32_t max_blocks;
+    const uint16_t *q;        // [B][hq][d]
+    const int32_t *q_pos;     // [B]
+    int32_t batch;
+    int32_t hq, hkv, group;
+    const float *cos_tab;
+    const float *sin_tab;
+    int32_t max_pos;
+    float scale_log2;
+    int32_t max_kv_len;
+    int32_t num_splits;
+    uint16_t *out;
+    float *lse;
+    float *part_o;            // [num_splits][B][hq][d]
+    float *part_ml;           // [num_splits][B][hq][2]
+};
+
+struct MergeParams {
+    const float *part_o;      // may be null (lse-only partials)
+    const float *part_ml;
+    int32_t num_splits;
+    int32_t rows;             // total_q * hq
+    uint16_t *out;            // nullable
+    float *lse;               // nullable
+};
+
+struct SelectParams {
+    const float *mass_part;   // [B][hkv][row_blocks][mass_stride]
+    int32_t hkv, row_blocks, mass_stride;
+    const int32_t *q_start;
+    int32_t group, rows_per_block;
+    const int32_t *kv_len;
+    const int32_t *kv_pos;
+    int32_t kv_stride;        // max_blocks * 16
+    int32_t batch;
+    float *mass;              // [B][kv_stride]
+    const int32_t *span_req, *span_start, *span_len, *sel_off;
+    int32_t n_spans;
+    int32_t *sel_idx;
+    int32_t max_sel;          // capacity of sel_idx (host value)
+};
+
+struct FuseParams {
+    uint16_t *k_pool;
+    uint16_t *v_pool;
+    int32_t num_blocks, hkv;
+    const int32_t *block_table;
+    int32_t *kv_len;
+    int32_t *kv_pos;
+    int32_t max_blocks;
+    const int32_t *sel_idx;
+    const int32_t *sel_req_off;
+    const uint16_t *k_new;
+    const uint16_t *v_new;
+    int32_t batch;
+    int32_t max_rows;         // bound of rows per request
+    int32_t n_sel;            // rows in k_new / v_new / sel_idx
+};
+
+// Launchers (return the launch's hipError_t).
+hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int qg, hipStream_t s);
+hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t s);
+hipError_t launch_merge(const MergeParams &p, int head_dim, hipStream_t s);
+hipError_t launch_mass_reduce(const SelectParams &p, hipStream_t s);
+hipError_t launch_topk(const SelectParams &p, hipStream_t s);
+hipError_t launch_fuse(const FuseParams &p, int head_dim, hipStream_t s);
+
+}  // namespace pic

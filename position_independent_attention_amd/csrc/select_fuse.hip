@@ -1,0 +1,239 @@
+// Query-centric selection and cache fusion for gfx950.
+//
+//   mass_reduce  sums the per-(kv head, row block) partial column masses that
+//                the mass pass writes, in a fixed order (deterministic), into
+//                mass[r][j] = sum over the request's query rows of the
+//                softmax probability of key j (QCFuse, gist.science
+//                2604.08585, methodology B: the query's attention over one
+//                layer's K picks the tokens to recompute).
+//   span_topk    one workgroup per span: radix select (4 x 8-bit digits of the
+//                fp32 bit pattern, which orders non-negative floats) of the
+//                k-th largest mass, then an in-order pass that keeps every
+//                larger key and the lowest-index keys equal to the threshold;
+//                output ascending.
+//   fuse_scatter writes recomputed K/V rows bit for bit into the
+//                request-private blocks appended after the sequence and
+//                rewrites pi (QCFuse "Lo esencial" step 4 / phase 4: recomputed
+//                tokens mixed into the stored cache; MiniPIC, gist.science
+//                2606.13126, section 2.1: shared blocks are never written).
+#include "pic_internal.h"
+
+namespace pic {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void mass_reduce_kernel(SelectParams p) {
+    const int r = blockIdx.y;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    int kvl = p.kv_len[r];
+    kvl = kvl < 0 ? 0 : (kvl > p.mass_stride ? p.mass_stride : kvl);
+    if (j >= kvl) return;
+    const int nrows = (p.q_start[r + 1] - p.q_start[r]) * p.group;
+    const int nrb = min(p.row_blocks, (nrows + p.rows_per_block - 1) / p.rows_per_block);
+    float s = 0.f;
+    for (int g = 0; g < p.hkv; ++g)
+        for (int rb = 0; rb < nrb; ++rb)
+            s += p.mass_part[(((size_t)r * p.hkv + g) * p.row_blocks + rb) * p.mass_stride + j];
+    p.mass[(size_t)r * p.kv_stride + j] = s;
+}
+
+// Exclusive prefix count of `flag` over the 256 threads, in thread order.
+// Returns the prefix; *total gets the workgroup total.  Uses s_cnt[4].
+__device__ __forceinline__ int block_excl_count(bool flag, int *s_cnt, int *total) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const unsigned long long m = __ballot(flag);
+    const int below = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) s_cnt[wave] = __popcll(m);
+    __syncthreads();
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int c = s_cnt[w];
+        pre += w < wave ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return pre + below;
+}
+
+__global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
+    __shared__ int s_hist[256];
+    __shared__ int s_cnt[4];
+    __shared__ uint32_t s_sel[2];
+    const int s = blockIdx.x, tid = threadIdx.x;
+    const int r = p.span_req[s], st = p.span_start[s], L = p.span_len[s];
+    const int k = p.sel_off[s + 1] - p.sel_off[s];
+    int32_t *out = p.sel_idx + p.sel_off[s];
+    if (r < 0 || r >= p.batch || k <= 0) return;
+    int kvl = p.kv_len[r];
+    kvl = kvl < 0 ? 0 : (kvl > p.kv_stride ? p.kv_stride : kvl);
+    const int lo = max(st, 0), hi = min(st + max(L, 0), kvl);
+    const int32_t *pis = p.kv_pos + (size_t)r * p.kv_stride;
+    const float *mass = p.mass + (size_t)r * p.kv_stride;
+
+    // candidates
+    int ncand = 0;
+    for (int base = lo; base < hi; base += 256) {
+        const int j = base + tid;
+        const bool c = j < hi && pis[j] >= 0;
+        int tot;
+        block_excl_count(c, s_cnt, &tot);
+        ncand += tot;
+    }
+    const int kk = min(k, ncand);
+    uint32_t thr = 0;
+    int take_eq = 0;
+    bool take_all = kk == ncand;
+    if (!take_all) {
+        uint32_t prefix = 0, pmask = 0;
+        int rem = kk;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            s_hist[tid] = 0;
+            __syncthreads();
+            for (int j = lo + tid; j < hi; j += 256) {
+                if (pis[j] < 0) continue;
+                const uint32_t key = __float_as_uint(mass[j]);
+                if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255], 1);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                int cum = 0, dsel = 0;
+                for (int d = 255; d >= 0; --d) {
+                    if (cum + s_hist[d] >= rem) {
+                        dsel = d;
+                        break;
+                    }
+                    cum += s_hist[d];
+                }
+                s_sel[0] = (uint32_t)dsel;
+                s_sel[1] = (uint32_t)(rem - cum);
+            }
+            __syncthreads();
+            prefix |= s_sel[0] << shift;
+            pmask |= 255u << shift;
+            rem = (int)s_sel[1];
+            __syncthreads();
+        }
+        thr = prefix;
+        take_eq = rem;
+    }
+    // in-order pass: larger than the threshold, or equal and among the first
+    // take_eq equal ones (lowest indices)
+    int out_base = 0, eq_base = 0;
+    for (int base = lo; base < hi; base += 256) {
+        const int j = base + tid;
+        bool cand = j < hi && pis[j] >= 0;
+        const uint32_t key = cand ? __float_as_uint(mass[j]) : 0u;
+        const bool gt = cand && (take_all || key > thr);
+        const bool eq = cand && !take_all && key == thr;
+        int eq_tot;
+        const int eq_rank = block_excl_count(eq, s_cnt, &eq_tot);
+        const bool take = gt || (eq && eq_base + eq_rank < take_eq);
+        int take_tot;
+        const int pos = block_excl_count(take, s_cnt, &take_tot);
+        if (take && p.sel_off[s] + out_base + pos < p.max_sel) out[out_base + pos] = j;
+        out_base += take_tot;
+        eq_base += eq_tot;
+    }
+    for (int i = kk + tid; i < k; i += 256)
+        if (p.sel_off[s] + i < p.max_sel) out[i] = -1;
+}
+
+// One workgroup per (fused block fb, kv head g, request r).
+template <int D>
+__global__ __launch_bounds__(256) void fuse_kernel(FuseParams p) {
+    __shared__ uint16_t s_v[16][D + 2];
+    const int fb = blockIdx.x, g = blockIdx.y, r = blockIdx.z, tid = threadIdx.x;
+    const int row0 = max(0, p.sel_req_off[r]);
+    const int cnt = min(p.sel_req_off[r + 1], p.n_sel) - row0;
+    const int kv_stride = p.max_blocks * kBlock;
+    int kvl = p.kv_len[r];
+    kvl = kvl < 0 ? 0 : (kvl > kv_stride ? kv_stride : kvl);
+    const int base = (kvl + kBlock - 1) / kBlock * kBlock;
+    int32_t *pis = p.kv_pos + (size_t)r * kv_stride;
+    if (fb == 0 && g == 0) {
+        for (int j = kvl + tid; j < base; j += 256) pis[j] = -1;
+    }
+    const int n_here = min(kBlock, cnt - kBlock * fb);
+    if (n_here <= 0) return;
+    const int bidx = base / kBlock + fb;
+    if (bidx >= p.max_blocks) return;
+    const int blk = p.block_table[(size_t)r * p.max_blocks + bidx];
+    if (blk < 0 || blk >= p.num_blocks) return;
+    const int rowb = row0 + kBlock * fb;
+
+    // K rows: token-major in the pool, 8 channels per task
+    for (int t = tid; t < kBlock * (D / 8); t += 256) {
+        const int sl = t / (D / 8), c = t % (D / 8);
+        if (sl < n_here) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(p.k_new + ((size_t)(rowb + sl) * p.hkv + g) * D + 8 * c);
+            *reinterpret_cast<u32x4 *>(p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + sl) * D + 8 * c) = v;
+        }
+    }
+    // V rows: stage token-major, write channel-major
+    for (int t = tid; t < kBlock * D; t += 256) {
+        const int sl = t / D, d = t % D;
+        s_v[sl][d] = sl < n_here ? p.v_new[((size_t)(rowb + sl) * p.hkv + g) * D + d] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int t = tid; t < kBlock * D; t += 256) {
+        const int d = t / kBlock, sl = t % kBlock;
+        if (sl < n_here) p.v_pool[(((size_t)blk * p.hkv + g) * D + d) * kBlock + sl] = s_v[sl][d];
+    }
+    // positions: fresh slot takes the stale slot's pi, the stale slot is masked
+    if (g == 0 && tid < n_here) {
+        const int i = kBlock * fb + tid;
+        const int sel = p.sel_idx[row0 + i];
+        const int slot = base + i;
+        if (sel >= 0 && sel < kvl) {
+            pis[slot] = pis[sel];
+            pis[sel] = -1;
+        } else {
+            pis[slot] = -1;
+        }
+    }
+}
+
+__global__ void fuse_len_kernel(FuseParams p) {
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= p.batch) return;
+    const int kv_stride = p.max_blocks * kBlock;
+    int kvl = p.kv_len[r];
+    kvl = kvl < 0 ? 0 : (kvl > kv_stride ? kv_stride : kvl);
+    const int base = (kvl + kBlock - 1) / kBlock * kBlock;
+    const int row0 = max(0, p.sel_req_off[r]);
+    const int cnt = max(0, min(p.sel_req_off[r + 1], p.n_sel) - row0);
+    p.kv_len[r] = min(base + cnt, kv_stride);
+}
+
+}  // namespace
+
+hipError_t launch_mass_reduce(const SelectParams &p, hipStream_t s) {
+    if (p.batch <= 0 || p.mass_stride <= 0) return hipSuccess;
+    hipLaunchKernelGGL(mass_reduce_kernel, dim3((p.mass_stride + 255) / 256, p.batch), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const SelectParams &p, hipStream_t s) {
+    if (p.n_spans <= 0) return hipSuccess;
+    hipLaunchKernelGGL(span_topk_kernel, dim3(p.n_spans), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_fuse(const FuseParams &p, int head_dim, hipStream_t s) {
+    if (p.batch <= 0) return hipSuccess;
+    const int nfb = p.max_rows > 0 ? (p.max_rows + kBlock - 1) / kBlock : 1;
+    const dim3 grid(nfb, p.hkv, p.batch);
+    if (head_dim == 64)
+        hipLaunchKernelGGL(fuse_kernel<64>, grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL(fuse_kernel<128>, grid, dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fuse_len_kernel, dim3((p.batch + 255) / 256), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace pic

@@ -1,0 +1,77 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and the host-only paths (status strings, selection budget, argument checks
+that return before any HIP call) behave as documented."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from position_independent_attention_amd import pic, workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    txt = open(os.path.join(ROOT, "include", "pic_attn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s*\b((?:pic|qc|kv)_\w+)\s*\(", txt, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 10, names
+    h = pic.lib()
+    for n in names:
+        assert hasattr(h, n), n
+
+
+def test_status_strings():
+    h = pic.lib()
+    assert h.pic_status_str(0) == b"PIC_OK"
+    assert h.pic_status_str(3) == b"PIC_ERR_WORKSPACE"
+    assert h.pic_status_str(99) == b"PIC_ERR_UNKNOWN"
+    assert h.pic_ctx_last_error(None) == b""
+
+
+@pytest.mark.parametrize("ratio", [0.0, 0.15, 0.25, 0.5, 1.0])
+def test_select_offsets_budget_matches_oracle(ratio):
+    lens = np.array([1024, 512, 128, 1, 3, 10, 0, 26, 7], np.int32)
+    off = pic.pic_select_offsets(lens, ratio)
+    w = W.custom(3, Hq=1, Hkv=1, d=4, theta=1e4, span_lens=[lens.tolist()], q_len=[1], ratio=ratio)
+    ref_off, _ = oracle.select(w, np.zeros(w.kv_pos.shape))
+    assert np.array_equal(off, ref_off)
+
+
+def test_select_offsets_rejects_bad_ratio():
+    with pytest.raises(pic.PicError):
+        pic.pic_select_offsets(np.array([4], np.int32), 1.5)
+
+
+@pytest.mark.parametrize("cfg,status", [
+    ((4, 1, 96, 16, 1024, 1e4), pic.PIC_ERR_UNSUPPORTED),     # head_dim
+    ((4, 1, 64, 8, 1024, 1e4), pic.PIC_ERR_UNSUPPORTED),      # block size
+    ((6, 4, 64, 16, 1024, 1e4), pic.PIC_ERR_INVALID_ARG),     # Hq % Hkv
+    ((4, 1, 64, 16, 0, 1e4), pic.PIC_ERR_INVALID_ARG),        # max_position
+    ((4, 1, 64, 16, 1024, -1.0), pic.PIC_ERR_INVALID_ARG),    # theta
+])
+def test_ctx_create_rejects_bad_config_before_touching_the_device(cfg, status):
+    c = pic.PicConfig(*cfg)
+    h = C.c_void_p()
+    assert pic.lib().pic_ctx_create(C.byref(c), C.byref(h)) == status
+    assert h.value is None
+
+
+def test_entry_points_reject_null_context():
+    h = pic.lib()
+    pool, req, qs, sp = pic.PicKvPool(), pic.PicReqTable(), pic.PicQueries(), pic.PicSpans()
+    assert h.pic_attn_prefill(None, C.byref(pool), C.byref(req), C.byref(qs), None, None, None, 0, None) == 1
+    assert h.pic_attn_decode(None, C.byref(pool), C.byref(req), None, None, None, None, None, 0, None) == 1
+    assert h.qc_score_select(None, C.byref(pool), C.byref(req), C.byref(qs), None, C.byref(sp), 0, None, None,
+                             None, 0, None) == 1
+    assert h.kv_fuse_scatter(None, C.byref(pool), C.byref(req), None, None, None, None, 0, 0, None) == 1
+    n = C.c_size_t()
+    assert h.pic_workspace_bytes(None, 0, C.byref(req), 0, 0, C.byref(n)) == 1

@@ -1,0 +1,385 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Bar: bf16 outputs max abs <= 2e-2 and mean abs <= 2e-3 (plus rel-L2 <= 1e-2);
+LSE abs <= 1e-3; selection mass abs <= 5e-4; selected sets identical outside
+a 1e-3 band around each span's k-th mass (ties to the lower index); fusion
+bit-exact.  Small shapes compare every output; the full-size shapes compare
+sampled rows and size-independent properties.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from position_independent_attention_amd import pic, workloads as W
+from tests import hip_helpers as H
+from tests.util import (LSE_ABS, MASS_ABS, check_selection, out_within, parity_stats)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(_):
+    H.require_gpu()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def edge_workloads():
+    return {
+        # kv_len not a multiple of 16 or 64, ragged spans, big position gaps
+        "ragged_gqa4_d128": lambda: W.custom(101, Hq=8, Hkv=2, d=128, theta=5e5,
+                                             span_lens=[[100, 37, 300], [5, 64]], gaps=[[0, 3000, 7], [40, 1]],
+                                             q_len=[19, 3], q_gap=[0, 50]),
+        "mha_d64": lambda: W.custom(102, Hq=4, Hkv=4, d=64, theta=1e4, span_lens=[[70, 90]], q_len=[33]),
+        "gqa8_d128": lambda: W.custom(103, Hq=16, Hkv=2, d=128, theta=5e5, span_lens=[[256, 128]], q_len=[40]),
+        "gqa1_q1": lambda: W.custom(104, Hq=2, Hkv=2, d=128, theta=1e4, span_lens=[[17], [300, 1]],
+                                    q_len=[1, 1]),
+        "many_rows": lambda: W.custom(105, Hq=32, Hkv=8, d=128, theta=5e5, span_lens=[[512, 257]],
+                                      q_len=[130]),
+        "batch3_zero_q": lambda: W.custom(106, Hq=8, Hkv=2, d=64, theta=1e4, span_lens=[[64], [80, 16], [33]],
+                                          q_len=[4, 0, 9]),
+    }
+
+
+def masked_inside_blocks():
+    w = W.custom(107, Hq=8, Hkv=2, d=128, theta=5e5, span_lens=[[200, 150]], q_len=[24], q_gap=[5])
+    rng = np.random.default_rng(7)
+    n = int(w.kv_len[0]) - 24
+    holes = rng.choice(n, size=60, replace=False)
+    w.kv_pos[0, holes] = -1
+    # garbage in a masked slot's V must not leak into the output
+    blk = w.block_table[0, holes[0] // 16]
+    w.pool_v[blk, :, :, holes[0] % 16] = 0x7fc0           # bf16 NaN
+    return w
+
+
+def compare_out(got, ref, what):
+    mx, mean, rel = parity_stats(got, ref)
+    say(f"  {what}: max {mx:.3e} mean {mean:.3e} rel {rel:.3e}")
+    assert out_within(got, ref), (what, mx, mean, rel)
+
+
+# --------------------------------------------------------------- prefill
+
+@pytest.mark.parametrize("name", ["tiny", "llama_layer"] + list(edge_workloads()) + ["masked_inside_blocks"])
+def test_prefill_parity(name):
+    w = {"tiny": W.tiny, "llama_layer": W.llama_layer, "masked_inside_blocks": masked_inside_blocks,
+         **edge_workloads()}[name]()
+    say(f"prefill {name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
+        f"kv={w.kv_len.tolist()} q={np.diff(w.q_start).tolist()}")
+    ctx = H.ctx_for(w)
+    out, lse, _ = H.prefill(ctx, w)
+    ref_o, ref_l = oracle.attention(w)
+    compare_out(H.host_bf16(out), ref_o, "O")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+
+
+def test_prefill_row_without_visible_keys():
+    w = W.custom(108, Hq=4, Hkv=1, d=64, theta=1e4, span_lens=[[40]], q_len=[3])
+    w.q_pos[0] = 0                     # its own key (pi = 0) is visible ...
+    n = int(w.kv_len[0])
+    w.kv_pos[0, n - 3] = 5             # ... unless it moves after the query
+    w.kv_pos[0, :40] += 10             # and the context too
+    ctx = H.ctx_for(w)
+    out, lse, _ = H.prefill(ctx, w)
+    o = H.host_bf16(out)
+    ref_o, ref_l = oracle.attention(w)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse.cpu().numpy()[0]))
+    assert np.all(np.isneginf(ref_l[0]))
+    compare_out(o, ref_o, "O")
+
+
+@pytest.mark.parametrize("name", ["shared_serving", "long_context"])
+def test_prefill_full_size_sampled(name):
+    w = {"shared_serving": W.shared_serving, "long_context": W.long_context}[name]()
+    say(f"prefill full {name}: B={w.batch} kv={w.max_kv_len} q={w.max_q_len}")
+    ctx = H.ctx_for(w)
+    out, lse, _ = H.prefill(ctx, w)
+    rng = np.random.default_rng(5)
+    nr = 48
+    reqs = rng.choice(w.batch, size=min(w.batch, 3), replace=False)
+    ts, hs = [], []
+    for i in range(nr):
+        r = reqs[i % len(reqs)]
+        ts.append(int(rng.integers(w.q_start[r], w.q_start[r + 1])))
+        hs.append(int(rng.integers(0, w.num_q_heads)))
+    ts[0], hs[0] = int(w.q_start[reqs[0]]), 0     # first query of a request (fewest own keys)
+    ref_o, ref_l = oracle.attention(w, (np.array(ts), np.array(hs)))
+    o = H.host_bf16(out)[ts, hs]
+    compare_out(o, ref_o, "O sampled")
+    assert np.max(np.abs(lse.cpu().numpy()[ts, hs] - ref_l)) <= LSE_ABS
+    assert np.all(np.isfinite(H.host_bf16(out)))
+
+
+# ---------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("name", ["small", "small_private", "edge_g8"])
+def test_decode_parity(name):
+    if name == "small":
+        w = W.decode_heavy(batch=5, n_spans=3, span_tok=80)
+    elif name == "small_private":
+        w = W.decode_heavy(batch=3, n_spans=2, span_tok=1024, private_spans=True, Hq=32)
+    else:
+        w = W.custom(109, Hq=16, Hkv=2, d=128, theta=5e5, span_lens=[[2500, 3], [1], [700, 700]],
+                     gaps=[[0, 9], [3], [0, 0]], q_len=[1, 1, 1], decode=True)
+        w.kv_pos[2, 100:140] = -1
+    say(f"decode {name}: B={w.batch} kv={w.kv_len.tolist()[:6]}")
+    ctx = H.ctx_for(w)
+    out, lse, _ = H.decode(ctx, w)
+    ref_o, ref_l = oracle.attention(w)
+    compare_out(H.host_bf16(out), ref_o, "O")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+
+
+def test_decode_full_size_sampled():
+    w = W.decode_heavy()
+    say(f"decode full: B={w.batch} kv={w.max_kv_len}")
+    ctx = H.ctx_for(w)
+    out, lse, _ = H.decode(ctx, w)
+    reqs = [0, 17, 63]
+    ts = np.repeat(reqs, w.num_q_heads)
+    hs = np.tile(np.arange(w.num_q_heads), len(reqs))
+    ref_o, ref_l = oracle.attention(w, (ts, hs))
+    compare_out(H.host_bf16(out)[ts, hs], ref_o, "O sampled")
+    assert np.max(np.abs(lse.cpu().numpy()[ts, hs] - ref_l)) <= LSE_ABS
+
+
+def test_decode_matches_prefill_with_one_query():
+    w = W.decode_heavy(batch=4, n_spans=2, span_tok=300)
+    ctx = H.ctx_for(w)
+    o1, l1, _ = H.decode(ctx, w)
+    o2, l2, _ = H.prefill(ctx, w)
+    a, b = H.host_bf16(o1), H.host_bf16(o2)
+    assert np.max(np.abs(a - b)) <= 1e-2
+    assert np.max(np.abs(l1.cpu().numpy() - l2.cpu().numpy())) <= 1e-4
+
+
+# ------------------------------------------------------------- selection
+
+def small_select_workloads():
+    return {
+        "tiny": W.tiny,
+        "llama_layer": W.llama_layer,
+        "long_context_small": lambda: W.long_context(n_spans=4, span_tok=512, q_len=64),
+        "shared_small": lambda: W.shared_serving(batch=3, n_pool_spans=6, span_tok=256, spans_per_req=3,
+                                                 q_len=32),
+        "edge_spans": lambda: W.custom(110, Hq=8, Hkv=2, d=64, theta=1e4, span_lens=[[1, 2, 300, 7], [45]],
+                                       q_len=[12, 5], ratio=0.34),
+    }
+
+
+@pytest.mark.parametrize("lse_given", [True, False])
+@pytest.mark.parametrize("name", list(small_select_workloads()))
+def test_select_parity(name, lse_given):
+    w = small_select_workloads()[name]()
+    say(f"select {name} lse_given={lse_given}: spans={len(w.span_req)} ratio={w.ratio}")
+    ctx = H.ctx_for(w)
+    out, lse, dc = H.prefill(ctx, w)
+    sel_off, sel, mass = H.select(ctx, w, dc, lse if lse_given else None)
+    ref_m = oracle.mass(w)
+    for r in range(w.batch):
+        n = int(w.kv_len[r])
+        err = np.max(np.abs(mass[r, :n] - ref_m[r, :n]))
+        say(f"  mass r{r}: max err {err:.3e} (sum {mass[r, :n].sum():.4f} vs {ref_m[r, :n].sum():.4f})")
+        assert err <= MASS_ABS
+    ref_off, ref_idx = oracle.select(w, ref_m)
+    check_selection(sel_off, sel, ref_off, ref_idx, ref_m, w)
+
+
+def test_select_ties_and_budget_edges():
+    """Equal masses (all-zero keys give every visible key the same weight)
+    resolve to the lower index; k = 0 and k = L spans."""
+    w = W.custom(111, Hq=4, Hkv=1, d=64, theta=1e4, span_lens=[[32, 32, 48]], q_len=[4], ratio=0.25)
+    w.pool_k[:] = 0
+    ctx = H.ctx_for(w)
+    _, lse, dc = H.prefill(ctx, w)
+    for ratio in (0.25, 0.0, 1.0):
+        sel_off, sel, mass = H.select(ctx, w, dc, lse, ratio=ratio)
+        ref_m = oracle.mass(w)
+        ref_off, ref_idx = oracle.select(w, ref_m, ratio)
+        assert np.array_equal(sel_off, ref_off)
+        assert np.array_equal(sel, ref_idx), (ratio, sel[:8], ref_idx[:8])
+
+
+def test_select_fewer_candidates_than_budget_pads_with_minus_one():
+    w = W.custom(112, Hq=4, Hkv=1, d=64, theta=1e4, span_lens=[[32]], q_len=[4], ratio=0.5)
+    w.kv_pos[0, 4:30] = -1                                 # 6 candidates left, budget 16
+    ctx = H.ctx_for(w)
+    _, lse, dc = H.prefill(ctx, w)
+    sel_off, sel, mass = H.select(ctx, w, dc, lse)
+    ref_m = oracle.mass(w)
+    ref_off, ref_idx = oracle.select(w, ref_m)
+    assert sel_off[-1] == 16 and len(ref_idx) == 6
+    assert np.array_equal(sel[:6], ref_idx) and np.all(sel[6:] == -1)
+
+
+def test_select_full_size_properties():
+    """Full 32k-context shape: every query row's probabilities sum to one, so
+    the mass sums to n_q * Hq; masked slots get none; the selection is the
+    per-span top-k of the returned mass with ties to the lower index."""
+    w = W.long_context()
+    ctx = H.ctx_for(w)
+    _, lse, dc = H.prefill(ctx, w)
+    sel_off, sel, mass = H.select(ctx, w, dc, lse)
+    n = int(w.kv_len[0])
+    total = float(mass[0, :n].astype(np.float64).sum())
+    say(f"select full: mass sum {total:.3f} expected {w.total_q * w.num_q_heads}")
+    assert abs(total - w.total_q * w.num_q_heads) <= 1e-4 * w.total_q * w.num_q_heads
+    assert np.all(mass[0, :n] >= 0)
+    for s in range(len(w.span_req)):
+        st, L = int(w.span_start[s]), int(w.span_len[s])
+        k = int(sel_off[s + 1] - sel_off[s])
+        order = sorted(range(st, st + L), key=lambda j: (-float(mass[0, j]), j))
+        assert list(sel[sel_off[s]:sel_off[s + 1]]) == sorted(order[:k])
+
+
+# ---------------------------------------------------------------- fusion
+
+@pytest.mark.parametrize("name", ["tiny", "shared_small", "edge_spans"])
+def test_fuse_bit_exact_and_second_pass(name):
+    """The oracle's own selection is fused by both sides: pool bytes, pi and
+    kv_len must match bit for bit, shared blocks stay untouched, and attention
+    over the fused cache matches the oracle over its fused copy."""
+    w = small_select_workloads()[name]()
+    ctx = H.ctx_for(w)
+    ref_m = oracle.mass(w)
+    ref_off, ref_idx = oracle.select(w, ref_m)
+    req_off = H.req_offsets(w, ref_off)
+    n = int(req_off[-1])
+    pk, pv, kp, kl = oracle.fuse(w, ref_idx, req_off, w.fresh_k[:n], w.fresh_v[:n])
+    dc = pic.to_device(w, H.DEV)
+    H.fuse(ctx, dc, ref_idx, req_off, w.fresh_k, w.fresh_v)
+    assert np.array_equal(dc.kv_len.cpu().numpy(), kl)
+    assert np.array_equal(dc.kv_pos.cpu().numpy(), kp)
+    gk = dc.pool_k.cpu().numpy().view(np.uint16)
+    gv = dc.pool_v.cpu().numpy().view(np.uint16)
+    assert np.array_equal(gk, pk) and np.array_equal(gv, pv)
+    assert np.array_equal(gk[w.shared_blocks], w.pool_k[w.shared_blocks])
+    fused = w.copy()
+    fused.pool_k, fused.pool_v, fused.kv_pos, fused.kv_len = pk, pv, kp, kl
+    dc.max_kv_len = int(kl.max())
+    out2, lse2, _ = H.prefill(ctx, fused, dc)
+    ref2, refl2 = oracle.attention(fused)
+    compare_out(H.host_bf16(out2), ref2, "O fused")
+    assert np.max(np.abs(lse2.cpu().numpy() - refl2)) <= LSE_ABS
+
+
+def test_fuse_full_size_with_seeded_selection():
+    """Full 32k shape: a seeded selection (15% per span, from the test's own
+    generator) fused on both sides; bitwise equal; then sampled rows of the
+    second pass against the oracle over its fused copy."""
+    w = W.long_context()
+    ctx = H.ctx_for(w)
+    rng = np.random.default_rng(44)
+    sel = np.concatenate([np.sort(rng.choice(np.arange(st, st + L), size=154, replace=False))
+                          for st, L in zip(w.span_start, w.span_len)]).astype(np.int32)
+    req_off = np.array([0, len(sel)], np.int32)
+    pk, pv, kp, kl = oracle.fuse(w, sel, req_off, w.fresh_k[:len(sel)], w.fresh_v[:len(sel)])
+    dc = pic.to_device(w, H.DEV)
+    H.fuse(ctx, dc, sel, req_off, w.fresh_k, w.fresh_v)
+    assert np.array_equal(dc.kv_len.cpu().numpy(), kl) and np.array_equal(dc.kv_pos.cpu().numpy(), kp)
+    assert np.array_equal(dc.pool_k.cpu().numpy().view(np.uint16), pk)
+    assert np.array_equal(dc.pool_v.cpu().numpy().view(np.uint16), pv)
+    fused = w.copy()
+    fused.pool_k, fused.pool_v, fused.kv_pos, fused.kv_len = pk, pv, kp, kl
+    dc.max_kv_len = int(kl.max())
+    out2, lse2, _ = H.prefill(ctx, fused, dc)
+    ts = np.array([0, 1, 77, 128, 255, 200, 31, 64])
+    hs = np.array([0, 31, 5, 17, 9, 22, 3, 12])
+    ref2, refl2 = oracle.attention(fused, (ts, hs))
+    compare_out(H.host_bf16(out2)[ts, hs], ref2, "O fused sampled")
+    assert np.max(np.abs(lse2.cpu().numpy()[ts, hs] - refl2)) <= LSE_ABS
+
+
+# ------------------------------------------------------- sharing / repeat
+
+def test_shared_pool_untouched_and_runs_bitwise_repeatable():
+    w = W.shared_serving(batch=4, n_pool_spans=8, span_tok=256, spans_per_req=4, q_len=48)
+    ctx = H.ctx_for(w)
+    dc = pic.to_device(w, H.DEV)
+    ck = dc.pool_k.clone()
+    cv = dc.pool_v.clone()
+    o1, l1, _ = H.prefill(ctx, w, dc)
+    s1 = H.select(ctx, w, dc, l1)
+    o2, l2, _ = H.prefill(ctx, w, dc)
+    s2 = H.select(ctx, w, dc, l2)
+    od1, ld1, _ = H.decode(ctx, _last_token_decode(w), None)
+    od2, ld2, _ = H.decode(ctx, _last_token_decode(w), None)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert np.array_equal(s1[1], s2[1]) and np.array_equal(s1[2], s2[2])
+    assert torch.equal(od1, od2) and torch.equal(ld1, ld2)
+    assert torch.equal(ck, dc.pool_k) and torch.equal(cv, dc.pool_v)
+
+
+def _last_token_decode(w):
+    """The same requests with only their last query token (decode shape)."""
+    d = w.copy()
+    last = w.q_start[1:] - 1
+    d.q = w.q[last]
+    d.q_pos = w.q_pos[last]
+    d.q_start = np.arange(w.batch + 1, dtype=np.int32)
+    return d
+
+
+def test_shared_blocks_at_different_offsets_match_private_copies():
+    """Two requests reading the same physical blocks at different logical
+    offsets give what each would get from private copies of those blocks."""
+    w = W.shared_serving(batch=2, n_pool_spans=3, span_tok=128, spans_per_req=3, q_len=16, seed=77)
+    ctx = H.ctx_for(w)
+    out, lse, _ = H.prefill(ctx, w)
+    for r in range(2):
+        solo = W.custom(0, Hq=w.num_q_heads, Hkv=w.num_kv_heads, d=w.head_dim, theta=w.rope_theta,
+                        span_lens=[[128] * 3], q_len=[16])
+        n = int(w.kv_len[r])
+        nb = (n + 15) // 16
+        solo.pool_k = np.ascontiguousarray(w.pool_k[w.block_table[r, :nb]])
+        solo.pool_v = np.ascontiguousarray(w.pool_v[w.block_table[r, :nb]])
+        solo.block_table = np.arange(nb, dtype=np.int32)[None, :]
+        solo.kv_pos = w.kv_pos[r:r + 1, :nb * 16].copy()
+        solo.kv_len = w.kv_len[r:r + 1].copy()
+        sl = slice(w.q_start[r], w.q_start[r + 1])
+        solo.q, solo.q_pos = w.q[sl].copy(), w.q_pos[sl].copy()
+        solo.q_start = np.array([0, 16], np.int32)
+        o2, l2, _ = H.prefill(ctx, solo)
+        # equal up to the split-merge order, which depends on the batch size
+        assert np.max(np.abs(H.host_bf16(out[sl]) - H.host_bf16(o2))) <= 1e-2
+        assert np.max(np.abs(lse[sl].cpu().numpy() - l2.cpu().numpy())) <= 1e-4
+
+
+# ------------------------------------------------------------ validation
+
+def test_argument_errors_return_status_before_launch():
+    w = W.tiny()
+    ctx = H.ctx_for(w)
+    dc = pic.to_device(w, H.DEV)
+    out = torch.empty(w.q.shape, dtype=torch.int16, device=H.DEV)
+    pool, req, qs = dc.pool(), dc.req(), dc.queries()
+    h = pic.lib()
+    import ctypes as C
+    bad = pic.PicReqTable(req.batch, req.max_blocks, req.max_blocks * 16 + 1, req.block_table, req.kv_len,
+                          req.kv_pos)
+    assert h.pic_attn_prefill(ctx.handle, C.byref(pool), C.byref(bad), C.byref(qs), out.data_ptr(), None,
+                              None, 0, None) == pic.PIC_ERR_INVALID_ARG
+    bigq = pic.PicQueries(qs.q, qs.q_start, qs.q_pos, qs.total_q, qs.total_q + 1)
+    assert h.pic_attn_prefill(ctx.handle, C.byref(pool), C.byref(req), C.byref(bigq), out.data_ptr(), None,
+                              None, 0, None) == pic.PIC_ERR_INVALID_ARG
+    # a workspace-needing shape without workspace
+    wl = W.llama_layer()
+    ctx2 = H.ctx_for(wl)
+    dc2 = pic.to_device(wl, H.DEV)
+    need = pic.pic_workspace_bytes(ctx2, pic.PIC_OP_PREFILL, dc2.req(), dc2.total_q, dc2.max_q_len)
+    assert need > 0
+    out2 = torch.empty(wl.q.shape, dtype=torch.int16, device=H.DEV)
+    assert h.pic_attn_prefill(ctx2.handle, C.byref(dc2.pool()), C.byref(dc2.req()), C.byref(dc2.queries()),
+                              out2.data_ptr(), None, None, 0, None) == pic.PIC_ERR_WORKSPACE
+    assert "workspace" in ctx2.last_error()
+    # decode with more than 16 q heads per kv head is declined
+    ctx3 = pic.Context(64, 2, 128, 1e4, 1024)
+    assert h.pic_attn_decode(ctx3.handle, C.byref(pool), C.byref(req), qs.q, qs.q_pos, out.data_ptr(), None,
+                             None, 0, None) == pic.PIC_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
