@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Throughput of the position-independent attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input (long-context
+query-centric fusion shape: 1 request, 32 reused 1024-token spans at shuffled
+logical offsets + 256 own query tokens = 33,024 KV slots, 32 q / 8 kv heads,
+d = 128, theta 5e5):
+  1. pic_attn_prefill   attention of the 256 queries with RoPE in-kernel, O + LSE
+  2. qc_score_select    per-key softmax mass from the same scores, top 15% per span
+  3. kv_fuse_scatter    4,928 recomputed K/V rows into request-private blocks
+  4. pic_attn_prefill   attention over the fused cache
+  5. pic_attn_decode    one generated token over the fused cache
+(plus two small device copies that restore the un-fused pi / kv_len so that
+every step starts from the same cache).
+
+metric: attended KV tokens per second, where each attention-type call over a
+request attends its kv_len minus masked slots (33,024 here) and the step makes
+four such calls.  The roofline object is for the dominant kernel (step 1,
+MFMA-bound: visible (query, key) pairs x Hq x 4d flops against the bf16 dense
+peak), timed with HIP events on the launch stream.  A decode-heavy line (64
+requests x 16,385 KV slots from 16 shared spans, 64 q / 8 kv heads) reports
+HBM-roofline throughput of pic_attn_decode.  cpu_baseline is the double-
+precision CPU oracle, single-threaded, timed on a sample of step 1's rows and
+scaled by visible (row, key) pairs to the whole step.
+
+    python bench.py [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attended KV tokens/s + % of HBM/MFMA roofline (GQA 32q/8kv, d=128)"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(w):
+    """Number of visible (query token, key) pairs per q head over all requests."""
+    tot = 0
+    for r in range(w.batch):
+        pi = w.kv_pos[r, :w.kv_len[r]]
+        pi = np.sort(pi[pi >= 0])
+        qp = w.q_pos[w.q_start[r]:w.q_start[r + 1]]
+        tot += int(np.searchsorted(pi, qp, side="right").sum())
+    return tot
+
+
+def attended_tokens(w):
+    return int(sum(int((w.kv_pos[r, :w.kv_len[r]] >= 0).sum()) for r in range(w.batch)))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-private", action="store_true",
+                    help="decode line on the unshared control (4 GiB pool)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see the design notes "
+              "for how it would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from position_independent_attention_amd import pic, workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    w = W.long_context()
+    log(f"workload built in {time.time() - t0:.1f}s: kv_len {w.max_kv_len}, q {w.total_q}")
+    ctx = pic.Context(w.num_q_heads, w.num_kv_heads, w.head_dim, w.rope_theta, w.max_position)
+    sel_off = pic.pic_select_offsets(w.span_len, w.ratio)
+    nsel = int(sel_off[-1])
+    dc = pic.to_device(w, dev, sel_off=sel_off)
+    kv0 = dc.max_kv_len
+    kv_fused = ((kv0 + 15) // 16) * 16 + nsel
+    kv_pos0 = dc.kv_pos.clone()
+    kv_len0 = dc.kv_len.clone()
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    out1 = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.int16, device=dev)
+    lse1 = torch.empty((w.total_q, w.num_q_heads), dtype=torch.float32, device=dev)
+    out2 = torch.empty_like(out1)
+    sel = torch.empty(nsel, dtype=torch.int32, device=dev)
+    req_off = t(np.array([0, nsel], np.int32))
+    fk, fv = t(w.fresh_k[:nsel]), t(w.fresh_v[:nsel])
+    q_dec = dc.q[-1:].clone()
+    qpos_dec = t(np.array([int(w.q_pos[-1]) + 1], np.int32))
+    out3 = torch.empty_like(q_dec)
+    dcd = pic.DeviceCache(dc.pool_k, dc.pool_v, dc.block_table, dc.kv_len, dc.kv_pos, kv_fused)
+
+    req_fused = pic.PicReqTable(1, dc.block_table.shape[1], kv_fused, 0, 0, 0)
+    need = max(
+        pic.pic_workspace_bytes(ctx, pic.PIC_OP_PREFILL, dc.req(), dc.total_q, dc.max_q_len),
+        pic.pic_workspace_bytes(ctx, pic.PIC_OP_PREFILL, req_fused, dc.total_q, dc.max_q_len),
+        pic.pic_workspace_bytes(ctx, pic.PIC_OP_SELECT, dc.req(), dc.total_q, dc.max_q_len),
+        pic.pic_workspace_bytes(ctx, pic.PIC_OP_DECODE, req_fused, 0, 0))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    names = ["prefill", "select", "fuse", "prefill_fused", "decode"]
+
+    def step(evs=None):
+        dc.kv_pos.copy_(kv_pos0)
+        dc.kv_len.copy_(kv_len0)
+        dc.max_kv_len = kv0
+        if evs: evs[0].record(stream)
+        pic.pic_attn_prefill(ctx, dc, out1, lse1, ws=ws, stream=stream)
+        if evs: evs[1].record(stream)
+        pic.qc_score_select(ctx, dc, lse1, nsel, sel, None, ws=ws, stream=stream)
+        if evs: evs[2].record(stream)
+        pic.kv_fuse_scatter(ctx, dc, sel, req_off, fk, fv, nsel, nsel, stream=stream)
+        if evs: evs[3].record(stream)
+        dc.max_kv_len = kv_fused
+        pic.pic_attn_prefill(ctx, dc, out2, None, ws=ws, stream=stream)
+        if evs: evs[4].record(stream)
+        pic.pic_attn_decode(ctx, dcd, q_dec, qpos_dec, out3, None, ws=ws, stream=stream)
+        if evs: evs[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    op_ms = {n: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+             for i, n in enumerate(names)}
+    log("per-op ms:", {k: round(v, 4) for k, v in op_ms.items()})
+
+    tokens = attended_tokens(w)
+    step_tokens = 4 * tokens
+    value = step_tokens / (ms_per_step / 1e3)
+    pairs = visible_pairs(w)
+    flops = pairs * w.num_q_heads * 4 * w.head_dim
+    achieved = flops / (op_ms["prefill"] / 1e3) / 1e12
+    roofline = {"kernel": "pic_attn_prefill (fwd_kernel<128,4,attn> + split merge), step 1",
+                "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops": flops, "avg_ms": round(op_ms["prefill"], 5)}
+
+    result = {"metric": METRIC, "value": round(value, 1), "unit": "attended KV tokens/s", "n_gpus": 1,
+              "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic",
+              "config": {"workload": "long_context_qc_fusion", "batch": 1, "kv_slots": int(w.max_kv_len),
+                         "spans": "32 x 1024 reused at shuffled offsets", "query_tokens": int(w.total_q),
+                         "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                         "rope_theta": w.rope_theta, "select_ratio": w.ratio, "fused_rows": nsel,
+                         "step": "prefill+lse, qc_score_select, kv_fuse_scatter, prefill(fused), decode(1)"},
+              "roofline": roofline, "ops_ms": {k: round(v, 5) for k, v in op_ms.items()}}
+
+    if not args.no_decode:
+        wd = W.decode_heavy(private_spans=args.decode_private)
+        ctxd = pic.Context(wd.num_q_heads, wd.num_kv_heads, wd.head_dim, wd.rope_theta, wd.max_position)
+        dd = pic.to_device(wd, dev)
+        outd = torch.empty((wd.batch, wd.num_q_heads, wd.head_dim), dtype=torch.int16, device=dev)
+        wsd = torch.empty(max(1, pic.pic_workspace_bytes(ctxd, pic.PIC_OP_DECODE, dd.req(), 0, 0)),
+                          dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            pic.pic_attn_decode(ctxd, dd, dd.q, dd.q_pos, outd, None, ws=wsd, stream=stream)
+        torch.cuda.synchronize()
+        reps = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            pic.pic_attn_decode(ctxd, dd, dd.q, dd.q_pos, outd, None, ws=wsd, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / reps
+        dtok = attended_tokens(wd)
+        kvbytes = dtok * wd.num_kv_heads * wd.head_dim * 2 * 2
+        result["decode_heavy"] = {
+            "workload": "decode_heavy" + ("_private" if args.decode_private else "") +
+                        ": 64 requests x 16,385 KV slots, 64 q / 8 kv heads, d 128",
+            "ms_per_call": round(dms, 5), "attended_kv_tokens_per_s": round(dtok / (dms / 1e3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(kvbytes / (dms / 1e3) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(kvbytes / (dms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes": kvbytes}}
+        del dd, outd, wsd
+        ctxd.close()
+
+    if not args.no_cpu_baseline:
+        import oracle
+        nt = min(args.cpu_sample_tokens, w.total_q)
+        ts = np.repeat(np.arange(nt), w.num_q_heads)
+        hs = np.tile(np.arange(w.num_q_heads), nt)
+        c0 = time.perf_counter()
+        oracle.attention(w, (ts, hs))
+        csec = time.perf_counter() - c0
+        pi = np.sort(w.kv_pos[0, :w.kv_len[0]][w.kv_pos[0, :w.kv_len[0]] >= 0])
+        sample_pairs = int(np.searchsorted(pi, w.q_pos[:nt], side="right").sum()) * w.num_q_heads
+        step_pairs = 3 * pairs * w.num_q_heads + tokens * w.num_q_heads   # 3 prefill-shaped passes + decode
+        cpu_step_s = csec * step_pairs / sample_pairs
+        result["cpu_baseline"] = {
+            "value": round(step_tokens / cpu_step_s, 2), "unit": "attended KV tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle.attention on {nt} query tokens x {w.num_q_heads} heads of step 1 at the full "
+                      f"33,024-slot context ({csec:.1f} s), scaled by visible (row, key) pairs to the whole step"}
+    ctx.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
