@@ -17,6 +17,7 @@ struct pic_ctx {
     pic_config cfg{};
     float *cos_d = nullptr;
     float *sin_d = nullptr;
+    uint16_t *zero_d = nullptr;   // zero page read in place of unusable keys
     std::string err;
 };
 
@@ -25,7 +26,7 @@ namespace {
 using pic::kBlock;
 
 constexpr size_t kAlign = 256;
-constexpr int kTargetWorkgroups = 512;   // >= 2 per CU on a 256-CU part
+constexpr int kCUs = 256;   // compute units of an MI355X
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -45,7 +46,7 @@ pic_status hip_fail(pic_ctx *ctx, hipError_t e, const char *where) {
 
 // Launch geometry of the prefill-style kernels.
 struct FwdPlan {
-    int qg = 1;           // 16-row MFMA column groups per wave
+    int shape = 0;        // kernel variant, see pic::fwd_rows_per_block
     int rows_per_block = 64;
     int row_blocks = 0;
     int split_len = pic::kTileN;
@@ -56,13 +57,15 @@ FwdPlan plan_fwd(const pic_config &c, int batch, int max_q_len, int max_kv_len) 
     FwdPlan pl;
     const int G = c.num_q_heads / c.num_kv_heads;
     const long long rows = (long long)max_q_len * G;
-    pl.qg = rows >= 256 ? 4 : (rows >= 128 ? 2 : 1);
-    pl.rows_per_block = 16 * pl.qg * pic::kWaves;
+    pl.shape = rows >= 128 ? 1 : 0;
+    pl.rows_per_block = pic::fwd_rows_per_block(c.head_dim, pl.shape);
     pl.row_blocks = (int)((rows + pl.rows_per_block - 1) / pl.rows_per_block);
     const long long base = (long long)pl.row_blocks * c.num_kv_heads * batch;
+    // the big shape runs one 512-thread workgroup per CU, the small one several
+    const long long target = pl.shape == 1 && c.head_dim == 128 ? kCUs : 2 * kCUs;
     int splits = 1;
     if (base > 0 && max_kv_len > 0) {
-        const long long want = (kTargetWorkgroups + base - 1) / base;
+        const long long want = (target + base - 1) / base;
         const long long cap = std::max(1, (max_kv_len + 255) / 256);   // >= 4 tiles per split
         splits = (int)std::max(1LL, std::min(want, cap));
     }
@@ -179,6 +182,7 @@ void fill_fwd_common(pic::FwdParams &p, const pic_ctx *ctx, const pic_kv_pool *p
     p.split_len = pl.split_len;
     p.num_splits = pl.num_splits;
     p.row_blocks = pl.row_blocks;
+    p.zero_page = ctx->zero_d;
 }
 
 }  // namespace
@@ -232,6 +236,9 @@ pic_status pic_ctx_create(const pic_config *cfg, pic_ctx **out) {
     if (e == hipSuccess) e = hipMalloc(&ctx->sin_d, n * sizeof(float));
     if (e == hipSuccess) e = hipMemcpy(ctx->cos_d, cs.data(), n * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(ctx->sin_d, sn.data(), n * sizeof(float), hipMemcpyHostToDevice);
+    const size_t zbytes = (size_t)cfg->head_dim * PIC_BLOCK_SIZE * sizeof(uint16_t);
+    if (e == hipSuccess) e = hipMalloc(&ctx->zero_d, zbytes);
+    if (e == hipSuccess) e = hipMemset(ctx->zero_d, 0, zbytes);
     if (e != hipSuccess) {
         pic_ctx_destroy(ctx);
         return PIC_ERR_HIP;
@@ -244,6 +251,7 @@ void pic_ctx_destroy(pic_ctx *ctx) {
     if (!ctx) return;
     if (ctx->cos_d) (void)hipFree(ctx->cos_d);
     if (ctx->sin_d) (void)hipFree(ctx->sin_d);
+    if (ctx->zero_d) (void)hipFree(ctx->zero_d);
     delete ctx;
 }
 
@@ -310,7 +318,7 @@ pic_status pic_attn_prefill(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req
         p.part_o = (float *)((char *)ws + w.part_o);
         p.part_ml = (float *)((char *)ws + w.part_ml);
     }
-    hipError_t e = pic::launch_fwd(p, c.head_dim, pic::kAttn, pl.qg, s);
+    hipError_t e = pic::launch_fwd(p, c.head_dim, pic::kAttn, pl.shape, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "prefill launch");
     if (pl.num_splits > 1) {
         pic::MergeParams m{p.part_o, p.part_ml, pl.num_splits, qs->total_q * c.num_q_heads, out, lse};
@@ -338,6 +346,7 @@ pic_status pic_attn_decode(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
     hipStream_t s = (hipStream_t)stream;
     pic::DecodeParams p;
     std::memset(&p, 0, sizeof p);
+    p.zero_page = ctx->zero_d;
     p.k_pool = pool->k;
     p.v_pool = pool->v;
     p.num_blocks = pool->num_blocks;
@@ -401,7 +410,7 @@ pic_status qc_score_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
         pic::FwdParams pl_lse = p;
         pl_lse.lse = lse_ws;
         if (pl.num_splits > 1) pl_lse.part_ml = (float *)(wb + w.lse_ml);
-        e = pic::launch_fwd(pl_lse, c.head_dim, pic::kLse, pl.qg, s);
+        e = pic::launch_fwd(pl_lse, c.head_dim, pic::kLse, pl.shape, s);
         if (e != hipSuccess) return hip_fail(ctx, e, "selection lse launch");
         if (pl.num_splits > 1) {
             pic::MergeParams m{nullptr, pl_lse.part_ml, pl.num_splits, qs->total_q * c.num_q_heads, nullptr, lse_ws};
@@ -438,7 +447,7 @@ pic_status qc_score_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
         pm.lse_in = lse_use;
         pm.mass_part = mass_part;
         pm.mass_stride = req->max_kv_len;
-        e = pic::launch_fwd(pm, c.head_dim, pic::kMass, pl.qg, s);
+        e = pic::launch_fwd(pm, c.head_dim, pic::kMass, pl.shape, s);
         if (e != hipSuccess) return hip_fail(ctx, e, "selection mass launch");
     }
     e = pic::launch_mass_reduce(sp, s);

@@ -22,12 +22,22 @@
 //   which leaves every lane with 8 consecutive keys: exactly the B operand
 //   layout that P^T needs for O^T += V^T P^T, with no shuffle.
 //
-//   Per 64-key tile the whole workgroup stages K once: global -> registers ->
-//   RoPE with the fp32 cos/sin table row of the key's pi -> bf16 -> LDS, so
-//   every key is rotated once per workgroup however many rows read it.  V is
-//   stored in the pool head-dim-major per block ([d][16]), so V^T tiles are
-//   plain 16-byte copies.  Global loads of the next tile are issued before the
-//   current tile's MFMA work.
+// Pipeline per 64-key tile (LDS double-buffered, one barrier per tile)
+//   - block ids and pi are loaded two tiles ahead, so the K / V / cos / sin
+//     loads of the next tile are issued at the top of the iteration without
+//     waiting on them;
+//   - the current tile is computed from LDS in two 32-key halves;
+//   - the next tile's K is rotated in registers with the fp32 cos/sin row of
+//     each key's pi (every key rotated once per workgroup however many rows
+//     read it), rounded to bf16 and written to the other LDS buffer with the
+//     V^T tile (a plain copy: V is stored head-dim-major per block);
+//   - the barrier also ANDs a per-thread "every key of the next tile is
+//     usable and visible to every row of the workgroup" flag, which selects a
+//     mask-free fast path.
+//   Softmax uses a lazy rescale: the running column max only moves (and O is
+//   rescaled) when a tile's max exceeds it by more than 2^8, so exp2 of
+//   (score*scale - max) stays below 256 and the O accumulator is almost never
+//   touched by VALU.
 #include "pic_internal.h"
 
 namespace pic {
@@ -38,6 +48,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kRescaleSlack = 8.0f;   // log2 units
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -82,112 +94,170 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
     return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
 }
 
-template <int D>
+// Column reductions over the 4 lane groups (16-lane rows) that hold the
+// same query column: v_permlane16_swap / v_permlane32_swap with both operands
+// equal leave the lane's value and its partner's in the two results.
+__device__ __forceinline__ float col_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int D, int WAVES>
 struct Geo {
+    static constexpr int NT = 64 * WAVES;        // threads per workgroup
     static constexpr int NC = D / 32;            // 32-wide MFMA k chunks along d
     static constexpr int HALF = D / 2;
     static constexpr int PC = D / 16;            // 8-pair chunks per key
-    static constexpr int KTASK = kTileN * PC / kThreads;   // K staging tasks per thread
-    static constexpr int VCH = D / 32;           // V chunks per thread
-    static constexpr int KS = D + 8;             // LDS row stride of K (bf16)
-    static constexpr int VS = kTileN + 8;        // LDS row stride of V^T (bf16)
+    static constexpr int KTASK = kTileN * PC / NT;   // K staging tasks per thread
+    static constexpr int VCH = 8 * D / NT;       // V 16-byte chunks per thread
+    static constexpr int KS = D;                 // LDS row stride of K (bf16), XOR-swizzled chunks
+    static constexpr int VS = kTileN + 8;        // LDS row stride of V^T (bf16), padded
+    static constexpr int KBUF = kTileN * KS;     // one K buffer (bf16 elements)
+    static constexpr int VBUF = D * VS;          // one V^T buffer
+    static_assert(KTASK >= 1 && VCH >= 1, "staging needs at least one task per thread");
 };
 
-// One thread's share of a tile's global loads, kept in registers while the
-// previous tile is being computed.
-template <int D>
-struct Stage {
-    u32x4 klo[Geo<D>::KTASK], khi[Geo<D>::KTASK];
-    int32_t kpi[Geo<D>::KTASK];     // pi if the key is usable, else -1
-    u32x4 v[Geo<D>::VCH];
-    int32_t vmask;                  // bit e set: key e of this thread's V chunk is unusable
+// K tile rows live in LDS with their 16-byte chunks permuted by
+// chunk ^ kswz(row): the 16 rows one MFMA operand read touches in a 16-lane
+// pass then cover all eight 16-byte bank groups twice (conflict-free).
+__device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
+
+// Block ids / positions of one tile for this thread's staging tasks.
+template <int D, int WAVES>
+struct Meta {
+    int32_t kblk[Geo<D, WAVES>::KTASK], kpi[Geo<D, WAVES>::KTASK];
+    int32_t vblk;
+    int32_t vpi[8];
 };
 
-template <int D>
-__device__ __forceinline__ void stage_load(const FwdParams &p, Stage<D> &st, int r, int g, int tile,
-                                           int key_end, int tid) {
-    using GG = Geo<D>;
-    const int32_t *bt = p.block_table + (size_t)r * p.max_blocks;
-    const int32_t *pis = p.kv_pos + (size_t)r * p.max_blocks * kBlock;
+// Data of one tile for this thread's staging tasks.
+template <int D, int WAVES>
+struct Data {
+    u32x4 klo[Geo<D, WAVES>::KTASK], khi[Geo<D, WAVES>::KTASK];
+    f32x4 cs[Geo<D, WAVES>::KTASK][4];     // cos0, cos1, sin0, sin1
+    int32_t kpi[Geo<D, WAVES>::KTASK];     // pi if the key is usable, else -1
+    u32x4 v[Geo<D, WAVES>::VCH];
+    int32_t vmask;                         // bit e: key e of the V chunk is unusable
+};
+
+// Unconditional loads at clamped indices, then select: no divergent branches.
+template <int D, int WAVES>
+__device__ __forceinline__ void meta_load(Meta<D, WAVES> &m, const int32_t *bt, const int32_t *pis, int tile,
+                                          int key_end, int tid) {
+    using GG = Geo<D, WAVES>;
+    const int last = key_end - 1;   // callers only load tiles with tile < key_end
 #pragma unroll
     for (int u = 0; u < GG::KTASK; ++u) {
-        const int kk = tid / GG::PC + u * (kThreads / GG::PC);
-        const int pc = tid % GG::PC;
-        const int j = tile + kk;
-        int pi = -1, blk = -1;
-        if (j < key_end) {
-            blk = bt[j >> 4];
-            pi = pis[j];
-        }
-        const bool ok = blk >= 0 && blk < p.num_blocks && pi >= 0 && pi < p.max_pos;
-        st.kpi[u] = ok ? pi : -1;
-        st.klo[u] = u32x4{0, 0, 0, 0};
-        st.khi[u] = u32x4{0, 0, 0, 0};
-        if (ok) {
-            const uint16_t *row = p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + (j & 15)) * D;
-            st.klo[u] = *reinterpret_cast<const u32x4 *>(row + 8 * pc);
-            st.khi[u] = *reinterpret_cast<const u32x4 *>(row + GG::HALF + 8 * pc);
-        }
+        const int j = tile + tid / GG::PC + u * (GG::NT / GG::PC);
+        const int jc = min(j, last);
+        const int b = bt[jc >> 4], pi = pis[jc];
+        m.kblk[u] = j <= last ? b : -1;
+        m.kpi[u] = j <= last ? pi : -1;
     }
-    // V^T chunks: this thread covers keys 16*b + 8*half .. +7 of the tile for
-    // d = dd + 32*u.
-    const int half = tid & 1, dd = (tid >> 1) & 31, b = (tid >> 6) & 3;
-    const int j0 = tile + 16 * b + 8 * half;
-    int blk = -1;
-    if (j0 < key_end) blk = bt[j0 >> 4];
-    const bool bok = blk >= 0 && blk < p.num_blocks;
-    int32_t vm = 0;
+    const int half = tid & 1, bq = (tid >> 6) & 3;
+    const int j0 = tile + 16 * bq + 8 * half;
+    const int b0 = bt[min(j0, last) >> 4];
+    m.vblk = j0 <= last ? b0 : -1;
+    if (j0 + 8 <= key_end) {
+        const i32x4 a = *reinterpret_cast<const i32x4 *>(pis + j0);
+        const i32x4 c = *reinterpret_cast<const i32x4 *>(pis + j0 + 4);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int j = j0 + e;
-        bool ok = bok && j < key_end;
-        if (ok) {
-            const int pi = pis[j];
-            ok = pi >= 0 && pi < p.max_pos;
+        for (int i = 0; i < 4; ++i) {
+            m.vpi[i] = a[i];
+            m.vpi[4 + i] = c[i];
         }
-        vm |= ok ? 0 : (1 << e);
-    }
-    st.vmask = vm;
+    } else {
 #pragma unroll
-    for (int u = 0; u < GG::VCH; ++u) {
-        const int d = dd + 32 * u;
-        st.v[u] = u32x4{0, 0, 0, 0};
-        if (bok && vm != 0xff)
-            st.v[u] = *reinterpret_cast<const u32x4 *>(
-                p.v_pool + (((size_t)blk * p.hkv + g) * D + d) * kBlock + 8 * half);
+        for (int e = 0; e < 8; ++e) {
+            const int v = pis[min(j0 + e, last)];
+            m.vpi[e] = j0 + e <= last ? v : -1;
+        }
     }
 }
 
-template <int D>
-__device__ __forceinline__ void stage_store(const FwdParams &p, Stage<D> &st, uint16_t *Ks,
-                                            uint16_t *Vs, int32_t *s_pi, int tid, bool need_v) {
-    using GG = Geo<D>;
-    const int half_n = GG::HALF;
+template <int D, int WAVES>
+__device__ __forceinline__ void data_load(const FwdParams &p, Data<D, WAVES> &dt, const Meta<D, WAVES> &m, int g,
+                                          int tile, int tid, bool need_v) {
+    using GG = Geo<D, WAVES>;
 #pragma unroll
     for (int u = 0; u < GG::KTASK; ++u) {
-        const int kk = tid / GG::PC + u * (kThreads / GG::PC);
+        const int kk = tid / GG::PC + u * (GG::NT / GG::PC);
         const int pc = tid % GG::PC;
-        const int pi = st.kpi[u];
-        u32x4 lo = st.klo[u], hi = st.khi[u];
-        if (pi >= 0) {
-            const float *cr = p.cos_tab + (size_t)pi * half_n + 8 * pc;
-            const float *sr = p.sin_tab + (size_t)pi * half_n + 8 * pc;
-            const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cr);
-            const f32x4 c1 = *reinterpret_cast<const f32x4 *>(cr + 4);
-            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sr);
-            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sr + 4);
-            rope8(lo, hi, c0, c1, s0, s1);
-        }
-        *reinterpret_cast<u32x4 *>(Ks + kk * GG::KS + 8 * pc) = lo;
-        *reinterpret_cast<u32x4 *>(Ks + kk * GG::KS + GG::HALF + 8 * pc) = hi;
+        const int j = tile + kk;
+        const int blk = m.kblk[u], pi = m.kpi[u];
+        const bool ok = blk >= 0 && blk < p.num_blocks && pi >= 0 && pi < p.max_pos;
+        dt.kpi[u] = ok ? pi : -1;
+        // unusable keys read the zero page: no branch, and they rotate to zero
+        const uint16_t *row = ok ? p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + (j & 15)) * D : p.zero_page;
+        dt.klo[u] = *reinterpret_cast<const u32x4 *>(row + 8 * pc);
+        dt.khi[u] = *reinterpret_cast<const u32x4 *>(row + GG::HALF + 8 * pc);
+    }
+    if (!need_v) return;
+    const int half = tid & 1, dd = (tid >> 1) & 31;
+    const bool bok = m.vblk >= 0 && m.vblk < p.num_blocks;
+    int32_t vm = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vm |= (bok && m.vpi[e] >= 0 && m.vpi[e] < p.max_pos) ? 0 : (1 << e);
+    dt.vmask = vm;
+    const uint16_t *vb = bok ? p.v_pool + ((size_t)m.vblk * p.hkv + g) * D * kBlock + 8 * half : p.zero_page;
+#pragma unroll
+    for (int u = 0; u < GG::VCH; ++u) {
+        const int d = dd + 32 * ((tid >> 8) + u * (GG::NT / 256));
+        dt.v[u] = *reinterpret_cast<const u32x4 *>(vb + (size_t)d * kBlock);
+    }
+}
+
+// cos/sin rows of the staged keys (row 0 for unusable keys, whose data is 0).
+template <int D, int WAVES>
+__device__ __forceinline__ void cs_load(const FwdParams &p, Data<D, WAVES> &dt, int tid) {
+    using GG = Geo<D, WAVES>;
+#pragma unroll
+    for (int u = 0; u < GG::KTASK; ++u) {
+        const int pc = tid % GG::PC;
+        const int pi = dt.kpi[u];
+        const float *cr = p.cos_tab + (size_t)(pi >= 0 ? pi : 0) * GG::HALF + 8 * pc;
+        const float *sr = p.sin_tab + (size_t)(pi >= 0 ? pi : 0) * GG::HALF + 8 * pc;
+        dt.cs[u][0] = *reinterpret_cast<const f32x4 *>(cr);
+        dt.cs[u][1] = *reinterpret_cast<const f32x4 *>(cr + 4);
+        dt.cs[u][2] = *reinterpret_cast<const f32x4 *>(sr);
+        dt.cs[u][3] = *reinterpret_cast<const f32x4 *>(sr + 4);
+    }
+}
+
+// Rotate and write one tile into an LDS buffer.  Returns whether every key
+// this thread staged is usable and visible to the workgroup's earliest row.
+template <int D, int WAVES>
+__device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uint16_t *Vs, int32_t *s_pi, int tid,
+                                           bool need_v, int min_pos) {
+    using GG = Geo<D, WAVES>;
+    bool full = true;
+#pragma unroll
+    for (int u = 0; u < GG::KTASK; ++u) {
+        const int kk = tid / GG::PC + u * (GG::NT / GG::PC);
+        const int pc = tid % GG::PC;
+        const int pi = dt.kpi[u];
+        u32x4 lo = dt.klo[u], hi = dt.khi[u];
+        rope8(lo, hi, dt.cs[u][0], dt.cs[u][1], dt.cs[u][2], dt.cs[u][3]);
+        const int sw = kswz(kk);
+        *reinterpret_cast<u32x4 *>(Ks + kk * GG::KS + 8 * (pc ^ sw)) = lo;
+        *reinterpret_cast<u32x4 *>(Ks + kk * GG::KS + 8 * ((pc + GG::HALF / 8) ^ sw)) = hi;
         if (pc == 0) s_pi[kk] = pi;
+        full = full && pi >= 0 && pi <= min_pos;
     }
     if (need_v) {
         const int half = tid & 1, dd = (tid >> 1) & 31, b = (tid >> 6) & 3;
-        const int vm = st.vmask;
+        const int vm = dt.vmask;
 #pragma unroll
         for (int u = 0; u < GG::VCH; ++u) {
-            u32x4 v = st.v[u];
+            u32x4 v = dt.v[u];
             if (vm) {   // zero unusable keys so that 0 * garbage cannot poison O
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -197,20 +267,23 @@ __device__ __forceinline__ void stage_store(const FwdParams &p, Stage<D> &st, ui
                     v[e] = w;
                 }
             }
-            const int d = dd + 32 * u;
+            const int d = dd + 32 * ((tid >> 8) + u * (GG::NT / 256));
             *reinterpret_cast<u32x4 *>(Vs + d * GG::VS + 16 * b + 8 * half) = v;
         }
     }
+    return full;
 }
 
-template <int D, int QG, int MODE>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
-    using GG = Geo<D>;
-    constexpr int BM = 16 * QG * kWaves;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kTileN * GG::KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[MODE == kAttn ? D * GG::VS : 8];
-    __shared__ int32_t s_pi[kTileN];
-    __shared__ float s_red[MODE == kMass ? kWaves * kTileN : 1];
+template <int D, int QG, int WAVES, int MODE>
+__global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
+    using GG = Geo<D, WAVES>;
+    constexpr int BM = 16 * QG * WAVES;
+    constexpr bool kV = MODE == kAttn;
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * GG::KBUF];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[kV ? 2 * GG::VBUF : 8];
+    __shared__ __attribute__((aligned(16))) int32_t s_pi[2 * kTileN];
+    __shared__ float s_red[MODE == kMass ? 2 * WAVES * kTileN : 1];
+    __shared__ int32_t s_minpos;
 
     const int nwg = p.row_blocks * p.hkv * p.num_splits * p.batch;
     int lid = xcd_remap(blockIdx.x, nwg);
@@ -231,15 +304,19 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
     kvl = kvl < 0 ? 0 : (kvl > kv_cap ? kv_cap : kvl);
     const int key_begin = sp * p.split_len;
     const int key_end = min(kvl, key_begin + p.split_len);
+    const int32_t *bt = p.block_table + (size_t)r * p.max_blocks;
+    const int32_t *pis = p.kv_pos + (size_t)r * kv_stride;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int lc = lane & 15, lg = lane >> 4;
+    if (tid == 0) s_minpos = 0x7fffffff;
 
     // ---- this lane's query columns: load, rotate at q_pos, keep as B operands
     u32x4 qop[QG][GG::NC];
     int qpos[QG], qt[QG], qh[QG];
     bool qvalid[QG];
+    int my_min = 0x7fffffff;
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
         const int row = rb * BM + wave * 16 * QG + 16 * qg + lc;
@@ -250,6 +327,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
         int pos = qvalid[qg] ? p.q_pos[qt[qg]] : -1;
         if (pos >= p.max_pos) pos = -1;
         qpos[qg] = pos;
+        if (qvalid[qg]) my_min = min(my_min, pos);
 #pragma unroll
         for (int c = 0; c < GG::NC; ++c) qop[qg][c] = u32x4{0, 0, 0, 0};
         if (pos >= 0) {
@@ -270,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
     }
 
     float m_run[QG], l_run[QG], lse2[QG];
-    f32x4 acc[MODE == kAttn ? QG : 1][MODE == kAttn ? D / 16 : 1];
+    f32x4 acc[kV ? QG : 1][kV ? D / 16 : 1];
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
         m_run[qg] = -INFINITY;
@@ -284,71 +362,137 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
             }
         }
     }
-    if constexpr (MODE == kAttn) {
+    if constexpr (kV) {
 #pragma unroll
         for (int qg = 0; qg < QG; ++qg)
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) acc[qg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    __syncthreads();
+    atomicMin(&s_minpos, my_min);
     const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
-    Stage<D> st;
-    if (ntiles > 0) stage_load<D>(p, st, r, g, key_begin, key_end, tid);
+    Meta<D, WAVES> m1, m2;
+    Data<D, WAVES> dnext;
+    bool full = false;
+    if (ntiles > 0) {
+        meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end, tid);
+        if (ntiles > 1) meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
+        data_load<D, WAVES>(p, dnext, m1, g, key_begin, tid, kV);
+        cs_load<D, WAVES>(p, dnext, tid);
+    }
+    __syncthreads();
+    const int min_pos = s_minpos;
+    if (ntiles > 0) {
+        const bool f = data_store<D, WAVES>(dnext, Ks, Vs, s_pi, tid, kV, min_pos);
+        full = __syncthreads_and(f);
+    }
+    const float sc = p.scale_log2;
 
     for (int it = 0; it < ntiles; ++it) {
+        const int cur = it & 1;
         const int tile = key_begin + it * kTileN;
-        __syncthreads();
-        stage_store<D>(p, st, Ks, Vs, s_pi, tid, MODE == kAttn);
-        __syncthreads();
-        if (it + 1 < ntiles) stage_load<D>(p, st, r, g, tile + kTileN, key_end, tid);
+        const uint16_t *Kc = Ks + cur * GG::KBUF;
+        const uint16_t *Vc = Vs + (kV ? cur * GG::VBUF : 0);
+        const int32_t *pc_ = s_pi + cur * kTileN;
+        const bool more = it + 1 < ntiles;
+        if (more) {
+            data_load<D, WAVES>(p, dnext, m2, g, tile + kTileN, tid, kV);
+            if (it + 2 < ntiles) meta_load<D, WAVES>(m2, bt, pis, tile + 2 * kTileN, key_end, tid);
+        }
 
-        // ---- S^T = K Q^T for the 64-key tile: sacc[qg][kh][T]
-        f32x4 sacc[QG][2][2];
+        float cs[16];   // kMass: column sums of this lane's 16 keys
+        if constexpr (MODE == kMass) {
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg)
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int T = 0; T < 2; ++T) sacc[qg][kh][T] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < 16; ++u) cs[u] = 0.f;
+        }
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
+            if (kh == 1 && more) cs_load<D, WAVES>(p, dnext, tid);
+            // ---- S^T = K Q^T for a 32-key half: sacc[qg][T]
+            f32x4 sacc[QG][2];
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) sacc[qg][0] = sacc[qg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int T = 0; T < 2; ++T) {
                 const int key = 32 * kh + 8 * (lc >> 2) + 4 * T + (lc & 3);
+                const int sw = kswz(key);
 #pragma unroll
                 for (int c = 0; c < GG::NC; ++c) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(Ks + key * GG::KS + 32 * c + 8 * lg);
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(Kc + key * GG::KS + 8 * ((4 * c + lg) ^ sw));
 #pragma unroll
-                    for (int qg = 0; qg < QG; ++qg) sacc[qg][kh][T] = mfma16(a, qop[qg][c], sacc[qg][kh][T]);
+                    for (int qg = 0; qg < QG; ++qg) sacc[qg][T] = mfma16(a, qop[qg][c], sacc[qg][T]);
                 }
             }
-        }
-        // pi of this lane's 16 keys: u = kh*8 + T*4 + i  ->  key 32kh + 8lg + 4T + i
-        int kp[16];
+            // pi of this lane's 8 keys (only read on tiles that need masking)
+            int kp[8];
+            if (!full) {
+                const i32x4 a = *reinterpret_cast<const i32x4 *>(pc_ + 32 * kh + 8 * lg);
+                const i32x4 b = *reinterpret_cast<const i32x4 *>(pc_ + 32 * kh + 8 * lg + 4);
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const i32x4 a = *reinterpret_cast<const i32x4 *>(s_pi + 32 * kh + 8 * lg);
-            const i32x4 b = *reinterpret_cast<const i32x4 *>(s_pi + 32 * kh + 8 * lg + 4);
+                for (int i = 0; i < 4; ++i) {
+                    kp[i] = a[i];
+                    kp[4 + i] = b[i];
+                }
+            }
+            u32x4 pb[kV ? QG : 1];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                kp[kh * 8 + i] = a[i];
-                kp[kh * 8 + 4 + i] = b[i];
+            for (int qg = 0; qg < QG; ++qg) {
+                float s[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[e] = sacc[qg][e >> 2][e & 3];
+                if (!full) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const bool vis = kp[e] >= 0 && kp[e] <= qpos[qg];
+                        s[e] = vis ? s[e] : -INFINITY;
+                    }
+                }
+                if constexpr (MODE == kMass) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) cs[kh * 8 + e] += fast_exp2(fmaf(s[e], sc, -lse2[qg]));
+                } else {
+                    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                                     fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+                    mx = col_max(mx);
+                    const float mxs = mx * sc;
+                    const bool need = mxs > m_run[qg] + kRescaleSlack;
+                    if (__any(need)) {
+                        const float m_new = need ? mxs : m_run[qg];
+                        const float alpha = need ? fast_exp2(m_run[qg] - m_new) : 1.f;
+                        m_run[qg] = m_new;
+                        l_run[qg] *= alpha;
+                        if constexpr (kV) {
+#pragma unroll
+                            for (int dt = 0; dt < D / 16; ++dt) acc[qg][dt] *= alpha;
+                        }
+                    }
+                    const float mu = m_run[qg] == -INFINITY ? 0.f : m_run[qg];
+                    float pr[8], ls = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        pr[e] = fast_exp2(fmaf(s[e], sc, -mu));
+                        ls += pr[e];
+                    }
+                    l_run[qg] += ls;
+                    if constexpr (kV) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) pb[qg][e] = pack2(pr[2 * e], pr[2 * e + 1]);
+                    }
+                }
+            }
+            if constexpr (kV) {
+                // ---- O^T += V^T P^T: one V operand feeds every column group
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) {
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(Vc + (16 * dt + lc) * GG::VS + 32 * kh + 8 * lg);
+#pragma unroll
+                    for (int qg = 0; qg < QG; ++qg) acc[qg][dt] = mfma16(a, pb[qg], acc[qg][dt]);
+                }
             }
         }
 
         if constexpr (MODE == kMass) {
-            float cs[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) cs[u] = 0.f;
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const float s = sacc[qg][u >> 3][(u >> 2) & 1][u & 3];
-                    const bool vis = kp[u] >= 0 && kp[u] <= qpos[qg];
-                    cs[u] += vis ? fast_exp2(s * p.scale_log2 - lse2[qg]) : 0.f;
-                }
-            }
             // Sum the 16 columns of the lane group: butterfly reduce-scatter,
             // afterwards lane lc holds the total of value index u = lc.
 #pragma unroll
@@ -362,56 +506,25 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
                 }
             }
             const int key = 32 * (lc >> 3) + 8 * lg + 4 * ((lc >> 2) & 1) + (lc & 3);
-            s_red[wave * kTileN + key] = cs[0];
-            __syncthreads();
+            s_red[(cur * WAVES + wave) * kTileN + key] = cs[0];
+        }
+
+        // ---- stage the next tile into the other buffer
+        bool f = true;
+        if (more)
+            f = data_store<D, WAVES>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs + (kV ? (cur ^ 1) * GG::VBUF : 0),
+                                     s_pi + (cur ^ 1) * kTileN, tid, kV, min_pos);
+        full = __syncthreads_and(f);
+
+        if constexpr (MODE == kMass) {
             if (tid < kTileN) {
-                const float tot = ((s_red[tid] + s_red[kTileN + tid]) + s_red[2 * kTileN + tid]) +
-                                  s_red[3 * kTileN + tid];
+                const float *sr = s_red + cur * WAVES * kTileN;
+                float tot = 0.f;
+#pragma unroll
+                for (int w = 0; w < WAVES; ++w) tot += sr[w * kTileN + tid];
                 const int j = tile + tid;
                 if (j < key_end)
                     p.mass_part[(((size_t)r * p.hkv + g) * p.row_blocks + rb) * p.mass_stride + j] = tot;
-            }
-        } else {
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-                float sv[16];
-                float mx = -INFINITY;
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const float s = sacc[qg][u >> 3][(u >> 2) & 1][u & 3];
-                    const bool vis = kp[u] >= 0 && kp[u] <= qpos[qg];
-                    sv[u] = vis ? s * p.scale_log2 : -INFINITY;
-                    mx = fmaxf(mx, sv[u]);
-                }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run[qg], mx);
-                const float m_use = m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = fast_exp2(m_run[qg] - m_use);
-                m_run[qg] = m_new;
-                float ls = 0.f;
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    sv[u] = fast_exp2(sv[u] - m_use);
-                    ls += sv[u];
-                }
-                l_run[qg] = l_run[qg] * alpha + ls;
-                if constexpr (MODE == kAttn) {
-#pragma unroll
-                    for (int dt = 0; dt < D / 16; ++dt) acc[qg][dt] *= alpha;
-#pragma unroll
-                    for (int kh = 0; kh < 2; ++kh) {
-                        u32x4 pb;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) pb[e] = pack2(sv[kh * 8 + 2 * e], sv[kh * 8 + 2 * e + 1]);
-#pragma unroll
-                        for (int dt = 0; dt < D / 16; ++dt) {
-                            const u32x4 a =
-                                *reinterpret_cast<const u32x4 *>(Vs + (16 * dt + lc) * GG::VS + 32 * kh + 8 * lg);
-                            acc[qg][dt] = mfma16(a, pb, acc[qg][dt]);
-                        }
-                    }
-                }
             }
         }
     }
@@ -420,14 +533,12 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
     // ---- epilogue: per-lane partial sums -> column totals
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
-        float lt = l_run[qg];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
+        const float lt = col_sum(l_run[qg]);
         if (!qvalid[qg]) continue;
         const size_t rowid = (size_t)qt[qg] * p.hq + qh[qg];
         if (p.num_splits == 1) {
             const bool any = lt > 0.f;
-            if constexpr (MODE == kAttn) {
+            if constexpr (kV) {
                 const float inv = any ? 1.f / lt : 0.f;
 #pragma unroll
                 for (int dt = 0; dt < D / 16; ++dt) {
@@ -442,13 +553,13 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
                 p.lse[rowid] = any ? (m_run[qg] + __log2f(lt)) * 0.6931471805599453f : -INFINITY;
         } else {
             const size_t prow = (size_t)sp * p.total_q * p.hq + rowid;
-            if constexpr (MODE == kAttn) {
+            if constexpr (kV) {
 #pragma unroll
                 for (int dt = 0; dt < D / 16; ++dt)
                     *reinterpret_cast<f32x4 *>(p.part_o + prow * D + 16 * dt + 4 * lg) = acc[qg][dt];
             }
             if (lg == 0) {
-                p.part_ml[prow * 2 + 0] = m_run[qg];
+                p.part_ml[prow * 2 + 0] = lt > 0.f ? m_run[qg] : -INFINITY;
                 p.part_ml[prow * 2 + 1] = lt;
             }
         }
@@ -485,36 +596,38 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     if (p.lse && part == 0) p.lse[row] = any ? (M + __log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
-template <int D, int QG, int MODE>
+template <int D, int QG, int WAVES, int MODE>
 hipError_t launch_one(const FwdParams &p, hipStream_t s) {
     const int nwg = p.row_blocks * p.hkv * p.num_splits * p.batch;
     if (nwg <= 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_kernel<D, QG, MODE>), dim3(nwg), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<D, QG, WAVES, MODE>), dim3(nwg), dim3(64 * WAVES), 0, s, p);
     return hipGetLastError();
 }
 
+// Variants: shape 0 = (QG 1, 4 waves): 64 rows per workgroup; shape 1 =
+// (QG 2, 8 waves): 256 rows at d = 128, (QG 2, 4 waves): 128 rows at d = 64.
 template <int D, int MODE>
-hipError_t launch_qg(const FwdParams &p, int qg, hipStream_t s) {
-    switch (qg) {
-    case 1: return launch_one<D, 1, MODE>(p, s);
-    case 2: return launch_one<D, 2, MODE>(p, s);
-    default: return launch_one<D, 4, MODE>(p, s);
-    }
+hipError_t launch_shape(const FwdParams &p, int shape, hipStream_t s) {
+    if (shape == 0) return launch_one<D, 1, 4, MODE>(p, s);
+    if constexpr (D == 128) return launch_one<D, 2, 8, MODE>(p, s);
+    else return launch_one<D, 2, 4, MODE>(p, s);
 }
 
 template <int D>
-hipError_t launch_mode(const FwdParams &p, int mode, int qg, hipStream_t s) {
+hipError_t launch_mode(const FwdParams &p, int mode, int shape, hipStream_t s) {
     switch (mode) {
-    case kAttn: return launch_qg<D, kAttn>(p, qg, s);
-    case kLse: return launch_qg<D, kLse>(p, qg, s);
-    default: return launch_qg<D, kMass>(p, qg, s);
+    case kAttn: return launch_shape<D, kAttn>(p, shape, s);
+    case kLse: return launch_shape<D, kLse>(p, shape, s);
+    default: return launch_shape<D, kMass>(p, shape, s);
     }
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int qg, hipStream_t s) {
-    return head_dim == 64 ? launch_mode<64>(p, mode, qg, s) : launch_mode<128>(p, mode, qg, s);
+int fwd_rows_per_block(int head_dim, int shape) { return shape == 0 ? 64 : (head_dim == 128 ? 256 : 128); }
+
+hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int shape, hipStream_t s) {
+    return head_dim == 64 ? launch_mode<64>(p, mode, shape, s) : launch_mode<128>(p, mode, shape, s);
 }
 
 hipError_t launch_merge(const MergeParams &p, int head_dim, hipStream_t s) {

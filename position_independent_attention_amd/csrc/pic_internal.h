@@ -17,6 +17,7 @@ enum Mode : int { kAttn = 0, kLse = 1, kMass = 2 };
 
 // Everything one prefill-style launch needs.  Pointers are device pointers.
 struct FwdParams {
+    const uint16_t *zero_page;  // >= 16*d zero bf16, read in place of unusable keys
     const uint16_t *k_pool;
     const uint16_t *v_pool;
     int32_t num_blocks;
@@ -49,6 +50,7 @@ struct FwdParams {
 };
 
 struct DecodeParams {
+    const uint16_t *zero_page;
     const uint16_t *k_pool;
     const uint16_t *v_pool;
     int32_t num_blocks;
@@ -115,7 +117,9 @@ struct FuseParams {
 };
 
 // Launchers (return the launch's hipError_t).
-hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int qg, hipStream_t s);
+// shape 0: 64 rows per workgroup; shape 1: 256 rows (d = 128) / 128 rows (d = 64)
+int fwd_rows_per_block(int head_dim, int shape);
+hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int shape, hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t s);
 hipError_t launch_merge(const MergeParams &p, int head_dim, hipStream_t s);
 hipError_t launch_mass_reduce(const SelectParams &p, hipStream_t s);
