@@ -5,7 +5,8 @@
 Each translation unit is compiled to an object in _build/ and linked into
 position_independent_attention_amd/libpicattn.so.  Flags: -O3, C++17,
 --offload-arch=gfx950, and the packed-fp32 target feature switched off for the
-device code (hipcc's host pass warns that it does not know the feature).
+device code (hipcc's host pass warns that it does not know the feature);
+-fno-honor-nans for the kernel sources.
 """
 from __future__ import annotations
 
@@ -29,11 +30,16 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+# Kernel sources only: no NaN canonicalisation before v_max (the kernels use
+# +-inf as sentinels but never rely on NaN semantics).  Host code keeps full
+# IEEE semantics for argument validation.
+KERNEL_FLAGS = ["-fno-honor-nans"]
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = KERNEL_FLAGS if src.endswith(".hip") else []
+    cmd = [HIPCC] + CFLAGS + extra + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

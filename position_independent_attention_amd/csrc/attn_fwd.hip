@@ -149,6 +149,8 @@ struct Data {
 };
 
 // Unconditional loads at clamped indices, then select: no divergent branches.
+// kv_stride (a multiple of 16) bounds every index: a V chunk's 8 positions
+// start at a multiple of 8 below key_end <= kv_stride, so they never cross it.
 template <int D, int WAVES>
 __device__ __forceinline__ void meta_load(Meta<D, WAVES> &m, const int32_t *bt, const int32_t *pis, int tile,
                                           int key_end, int tid) {
@@ -163,23 +165,16 @@ __device__ __forceinline__ void meta_load(Meta<D, WAVES> &m, const int32_t *bt, 
         m.kpi[u] = j <= last ? pi : -1;
     }
     const int half = tid & 1, bq = (tid >> 6) & 3;
-    const int j0 = tile + 16 * bq + 8 * half;
-    const int b0 = bt[min(j0, last) >> 4];
-    m.vblk = j0 <= last ? b0 : -1;
-    if (j0 + 8 <= key_end) {
-        const i32x4 a = *reinterpret_cast<const i32x4 *>(pis + j0);
-        const i32x4 c = *reinterpret_cast<const i32x4 *>(pis + j0 + 4);
+    const int j0 = min(tile + 16 * bq + 8 * half, last & ~7);
+    const bool in = tile + 16 * bq + 8 * half <= last;
+    const int b0 = bt[j0 >> 4];
+    m.vblk = in ? b0 : -1;
+    const i32x4 a = *reinterpret_cast<const i32x4 *>(pis + j0);
+    const i32x4 c = *reinterpret_cast<const i32x4 *>(pis + j0 + 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            m.vpi[i] = a[i];
-            m.vpi[4 + i] = c[i];
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int v = pis[min(j0 + e, last)];
-            m.vpi[e] = j0 + e <= last ? v : -1;
-        }
+    for (int i = 0; i < 4; ++i) {
+        m.vpi[i] = (in && j0 + i <= last) ? a[i] : -1;
+        m.vpi[4 + i] = (in && j0 + 4 + i <= last) ? c[i] : -1;
     }
 }
 
@@ -347,12 +342,20 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         }
     }
 
-    float m_run[QG], l_run[QG], lse2[QG];
+    // Running max in log2 units.  Starting from a finite -1e30 (instead of
+    // -inf) keeps exp2(s*scale - m) well defined without a select: the first
+    // visible score always triggers a rescale, and fully masked columns give
+    // exp2(-inf) = 0.
+    float m_run[QG], lse2[QG];
     f32x4 acc[kV ? QG : 1][kV ? D / 16 : 1];
+    // Row sums of P on the MFMA pipe: A = 16 x 32 with ones in row 0, so row 0
+    // of acc_l[qg] accumulates sum_k P^T[k][col] (lanes of group 0, element 0).
+    f32x4 acc_l[MODE == kMass ? 1 : QG];
+    const u32x4 ones_a = lc == 0 ? u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u} : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
-        m_run[qg] = -INFINITY;
-        l_run[qg] = 0.f;
+        m_run[qg] = -1e30f;
+        if constexpr (MODE != kMass) acc_l[qg] = f32x4{0.f, 0.f, 0.f, 0.f};
         lse2[qg] = INFINITY;
         if constexpr (MODE == kMass) {
             if (qpos[qg] >= 0) {
@@ -435,7 +438,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
                     kp[4 + i] = b[i];
                 }
             }
-            u32x4 pb[kV ? QG : 1];
+            u32x4 pb[QG];
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) {
                 float s[8];
@@ -461,25 +464,23 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
                         const float m_new = need ? mxs : m_run[qg];
                         const float alpha = need ? fast_exp2(m_run[qg] - m_new) : 1.f;
                         m_run[qg] = m_new;
-                        l_run[qg] *= alpha;
+                        acc_l[qg] *= alpha;
                         if constexpr (kV) {
 #pragma unroll
                             for (int dt = 0; dt < D / 16; ++dt) acc[qg][dt] *= alpha;
                         }
                     }
-                    const float mu = m_run[qg] == -INFINITY ? 0.f : m_run[qg];
-                    float pr[8], ls = 0.f;
+                    const float mu = m_run[qg];
+                    u32x4 pq;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        pr[e] = fast_exp2(fmaf(s[e], sc, -mu));
-                        ls += pr[e];
-                    }
-                    l_run[qg] += ls;
-                    if constexpr (kV) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) pb[qg][e] = pack2(pr[2 * e], pr[2 * e + 1]);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        pq[e] = pack2(fast_exp2(fmaf(s[2 * e], sc, -mu)), fast_exp2(fmaf(s[2 * e + 1], sc, -mu)));
+                    pb[qg] = pq;
                 }
+            }
+            if constexpr (MODE != kMass) {
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg) acc_l[qg] = mfma16(ones_a, pb[qg], acc_l[qg]);
             }
             if constexpr (kV) {
                 // ---- O^T += V^T P^T: one V operand feeds every column group
@@ -533,7 +534,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     // ---- epilogue: per-lane partial sums -> column totals
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
-        const float lt = col_sum(l_run[qg]);
+        const float lt = col_sum(acc_l[qg][0]);   // row 0 lives in lane group 0
         if (!qvalid[qg]) continue;
         const size_t rowid = (size_t)qt[qg] * p.hq + qh[qg];
         if (p.num_splits == 1) {

@@ -156,7 +156,8 @@ def test_decode_matches_prefill_with_one_query():
     o2, l2, _ = H.prefill(ctx, w)
     a, b = H.host_bf16(o1), H.host_bf16(o2)
     assert np.max(np.abs(a - b)) <= 1e-2
-    assert np.max(np.abs(l1.cpu().numpy() - l2.cpu().numpy())) <= 1e-4
+    # the prefill kernel sums bf16-rounded P (on the MFMA), decode sums fp32 p
+    assert np.max(np.abs(l1.cpu().numpy() - l2.cpu().numpy())) <= 2e-3
 
 
 # ------------------------------------------------------------- selection
