@@ -40,6 +40,8 @@
 //   touched by VALU.
 #include "pic_internal.h"
 
+#include <type_traits>
+
 namespace pic {
 namespace {
 
@@ -64,6 +66,21 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+#ifndef PIC_SCHED_HINTS
+#define PIC_SCHED_HINTS 0
+#endif
+// Ask the scheduler for `n` groups of (1 MFMA, v VALU) in the current region.
+template <int n, int v>
+__device__ __forceinline__ void interleave_hint() {
+#if PIC_SCHED_HINTS
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, v, 0);
+    }
+#endif
+}
 
 // Rotate 8 RoPE pairs: lo holds x[i..i+7], hi holds x[i+d/2..i+d/2+7] (bf16),
 // c/s the cos/sin of pos * theta^(-2(i+e)/d).  Result rounded to bf16.
@@ -118,24 +135,28 @@ struct Geo {
     static constexpr int PC = D / 16;            // 8-pair chunks per key
     static constexpr int KTASK = kTileN * PC / NT;   // K staging tasks per thread
     static constexpr int VCH = 8 * D / NT;       // V 16-byte chunks per thread
-    static constexpr int KS = D;                 // LDS row stride of K (bf16), XOR-swizzled chunks
+    static constexpr int KS = D + 8;             // LDS row stride of K (bf16), padded 16 B
     static constexpr int VS = kTileN + 8;        // LDS row stride of V^T (bf16), padded
     static constexpr int KBUF = kTileN * KS;     // one K buffer (bf16 elements)
     static constexpr int VBUF = D * VS;          // one V^T buffer
     static_assert(KTASK >= 1 && VCH >= 1, "staging needs at least one task per thread");
 };
 
-// K tile rows live in LDS with their 16-byte chunks permuted by
-// chunk ^ kswz(row): the 16 rows one MFMA operand read touches in a 16-lane
-// pass then cover all eight 16-byte bank groups twice (conflict-free).
-__device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
+// K tile key k = 32*kh + 8*a + 4*T + b lives in LDS row
+// krow(k) = 32*kh + 16*T + 4*a + b: the 16 keys that one MFMA operand read
+// takes (MFMA row m = 4a + b of tile T) are 16 consecutive rows, which the
+// 16-byte row padding spreads over all bank groups (conflict-free); the read
+// address is one per-lane base plus immediates.
+__device__ __forceinline__ int krow(int k) {
+    return (k & ~31) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
+}
 
 // Block ids / positions of one tile for this thread's staging tasks.
 template <int D, int WAVES>
 struct Meta {
     int32_t kblk[Geo<D, WAVES>::KTASK], kpi[Geo<D, WAVES>::KTASK];
     int32_t vblk;
-    int32_t vpi[8];
+    int32_t vkey_pi;   // lanes 0..15: pi of key lane of this wave's V block
 };
 
 // Data of one tile for this thread's staging tasks.
@@ -164,18 +185,14 @@ __device__ __forceinline__ void meta_load(Meta<D, WAVES> &m, const int32_t *bt, 
         m.kblk[u] = j <= last ? b : -1;
         m.kpi[u] = j <= last ? pi : -1;
     }
-    const int half = tid & 1, bq = (tid >> 6) & 3;
-    const int j0 = min(tile + 16 * bq + 8 * half, last & ~7);
-    const bool in = tile + 16 * bq + 8 * half <= last;
-    const int b0 = bt[j0 >> 4];
-    m.vblk = in ? b0 : -1;
-    const i32x4 a = *reinterpret_cast<const i32x4 *>(pis + j0);
-    const i32x4 c = *reinterpret_cast<const i32x4 *>(pis + j0 + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m.vpi[i] = (in && j0 + i <= last) ? a[i] : -1;
-        m.vpi[4 + i] = (in && j0 + 4 + i <= last) ? c[i] : -1;
-    }
+    // V staging: every lane of this wave covers keys of tile block (wave & 3)
+    const int bq = (tid >> 6) & 3;
+    const int jb = tile + 16 * bq;
+    const int b0 = bt[min(jb, last) >> 4];
+    m.vblk = jb <= last ? b0 : -1;
+    const int jl = jb + (tid & 15);
+    const int pl = pis[min(jl, last)];
+    m.vkey_pi = jl <= last ? pl : -1;
 }
 
 template <int D, int WAVES>
@@ -198,10 +215,12 @@ __device__ __forceinline__ void data_load(const FwdParams &p, Data<D, WAVES> &dt
     if (!need_v) return;
     const int half = tid & 1, dd = (tid >> 1) & 31;
     const bool bok = m.vblk >= 0 && m.vblk < p.num_blocks;
-    int32_t vm = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vm |= (bok && m.vpi[e] >= 0 && m.vpi[e] < p.max_pos) ? 0 : (1 << e);
-    dt.vmask = vm;
+    // validity of the block's 16 keys: lanes 0..15 hold their pi; the ballot
+    // lands in scalar registers
+    const bool kv_ok = m.vkey_pi >= 0 && m.vkey_pi < p.max_pos;
+    const uint32_t okmask = (uint32_t)__ballot(kv_ok) & 0xffffu;
+    dt.vmask = bok ? (int32_t)((~okmask >> (8 * half)) & 0xffu) : 0xff;
+    const int32_t vm = dt.vmask;
     const uint16_t *vb = bok ? p.v_pool + ((size_t)m.vblk * p.hkv + g) * D * kBlock + 8 * half : p.zero_page;
 #pragma unroll
     for (int u = 0; u < GG::VCH; ++u) {
@@ -241,27 +260,27 @@ __device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uin
         const int pi = dt.kpi[u];
         u32x4 lo = dt.klo[u], hi = dt.khi[u];
         rope8(lo, hi, dt.cs[u][0], dt.cs[u][1], dt.cs[u][2], dt.cs[u][3]);
-        const int sw = kswz(kk);
-        *reinterpret_cast<u32x4 *>(Ks + kk * GG::KS + 8 * (pc ^ sw)) = lo;
-        *reinterpret_cast<u32x4 *>(Ks + kk * GG::KS + 8 * ((pc + GG::HALF / 8) ^ sw)) = hi;
-        if (pc == 0) s_pi[kk] = pi;
+        const int kr = krow(kk);
+        *reinterpret_cast<u32x4 *>(Ks + kr * GG::KS + 8 * pc) = lo;
+        *reinterpret_cast<u32x4 *>(Ks + kr * GG::KS + GG::HALF + 8 * pc) = hi;
+        // masked-path visibility is one compare: unusable keys get INT_MAX
+        if (pc == 0) s_pi[kk] = pi >= 0 ? pi : 0x7fffffff;
         full = full && pi >= 0 && pi <= min_pos;
     }
     if (need_v) {
         const int half = tid & 1, dd = (tid >> 1) & 31, b = (tid >> 6) & 3;
         const int vm = dt.vmask;
+        // keep masks: unusable keys are zeroed so that 0 * garbage cannot
+        // poison O (branch-free: the staging sits inside an MFMA region)
+        uint32_t keep[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            keep[e] = ((vm >> (2 * e)) & 1 ? 0u : 0x0000ffffu) | ((vm >> (2 * e + 1)) & 1 ? 0u : 0xffff0000u);
 #pragma unroll
         for (int u = 0; u < GG::VCH; ++u) {
             u32x4 v = dt.v[u];
-            if (vm) {   // zero unusable keys so that 0 * garbage cannot poison O
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint32_t w = v[e];
-                    if (vm & (1 << (2 * e))) w &= 0xffff0000u;
-                    if (vm & (1 << (2 * e + 1))) w &= 0x0000ffffu;
-                    v[e] = w;
-                }
-            }
+            for (int e = 0; e < 4; ++e) v[e] &= keep[e];
             const int d = dd + 32 * ((tid >> 8) + u * (GG::NT / 256));
             *reinterpret_cast<u32x4 *>(Vs + d * GG::VS + 16 * b + 8 * half) = v;
         }
@@ -386,113 +405,191 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     }
     __syncthreads();
     const int min_pos = s_minpos;
+    // Is every key of this workgroup's range usable and visible to all of
+    // its rows?  (pi and block ids are small and L2-resident.)
+    bool my_ok = true;
+    for (int j = key_begin + tid; j < key_end; j += GG::NT) {
+        const int pi = pis[j], blk = bt[j >> 4];
+        my_ok = my_ok && pi >= 0 && pi < p.max_pos && pi <= min_pos && blk >= 0 && blk < p.num_blocks;
+    }
+    const bool wg_full = __syncthreads_and(my_ok);
     if (ntiles > 0) {
         const bool f = data_store<D, WAVES>(dnext, Ks, Vs, s_pi, tid, kV, min_pos);
         full = __syncthreads_and(f);
     }
+    (void)full;
     const float sc = p.scale_log2;
+    float m_ref[QG];                    // reference max of the next P half
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) m_ref[qg] = m_run[qg];
 
-    for (int it = 0; it < ntiles; ++it) {
+    // ---- software pipeline over 32-key halves.  Per tile:
+    //   R1  QK(half 1)            || softmax(half 0)
+    //   R2  PV(half 0)            || softmax(half 1)
+    //   R3  PV(half 1)            || rotate + stage the next tile
+    //   --  barrier
+    //   R4  QK(next tile, half 0)
+    // Every softmax uses the running max as it stood after the previous half
+    // (so the scores and the max reduction are independent of the MFMAs in
+    // flight); the O / row-sum rescale, when the max moved by more than 2^8,
+    // happens after that half's PV, outside the interleaved regions.  A half
+    // whose max jumps by more than 2^64 recomputes its P first (never taken
+    // for finite-range data, kept for safety).
+    auto qk_half = [&](const uint16_t *Kb, int kh, f32x4 (&sacc)[QG][2]) {
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) sacc[qg][0] = sacc[qg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // d-chunk outermost: 2*QG independent accumulators separate the
+        // dependent MFMAs of one accumulator chain
+        const uint16_t *k0 = Kb + (32 * kh + lc) * GG::KS + 8 * lg;   // krow of tile T = 0 keys
+        const uint16_t *k1 = k0 + 16 * GG::KS;                          // tile T = 1
+#pragma unroll
+        for (int c = 0; c < GG::NC; ++c) {
+            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(k0 + 32 * c);
+            const u32x4 a1 = *reinterpret_cast<const u32x4 *>(k1 + 32 * c);
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) {
+                sacc[qg][0] = mfma16(a0, qop[qg][c], sacc[qg][0]);
+                sacc[qg][1] = mfma16(a1, qop[qg][c], sacc[qg][1]);
+            }
+        }
+    };
+    // Scores of one half -> masked, scaled exp2 -> bf16 P^T operands (attn /
+    // lse) or column sums (mass).  Returns the scaled column maxima in mx.
+    auto softmax_half = [&](auto full_c, const f32x4 (&sacc)[QG][2], const int32_t *pib, int kh,
+                            u32x4 (&pb)[QG], float (&mx)[QG], float (&cs)[16]) {
+        constexpr bool FULL = decltype(full_c)::value;
+        int kp[8];
+        if constexpr (!FULL) {
+            const i32x4 a = *reinterpret_cast<const i32x4 *>(pib + 32 * kh + 8 * lg);
+            const i32x4 b = *reinterpret_cast<const i32x4 *>(pib + 32 * kh + 8 * lg + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kp[i] = a[i];
+                kp[4 + i] = b[i];
+            }
+        }
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+            float s[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[e] = sacc[qg][e >> 2][e & 3];
+            if constexpr (!FULL) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[e] = kp[e] <= qpos[qg] ? s[e] : -INFINITY;
+            }
+            if constexpr (MODE == kMass) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cs[kh * 8 + e] += fast_exp2(fmaf(s[e], sc, -lse2[qg]));
+            } else {
+                const float mu = m_ref[qg];
+                u32x4 pq;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    pq[e] = pack2(fast_exp2(fmaf(s[2 * e], sc, -mu)), fast_exp2(fmaf(s[2 * e + 1], sc, -mu)));
+                pb[qg] = pq;
+                const float m8 = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                                       fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+                mx[qg] = col_max(m8) * sc;
+            }
+        }
+    };
+    auto pv_half = [&](const uint16_t *Vb, int kh, const u32x4 (&pb)[QG]) {
+        if constexpr (MODE != kMass) {
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) acc_l[qg] = mfma16(ones_a, pb[qg], acc_l[qg]);
+        }
+        if constexpr (kV) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(Vb + (16 * dt + lc) * GG::VS + 32 * kh + 8 * lg);
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg) acc[qg][dt] = mfma16(a, pb[qg], acc[qg][dt]);
+            }
+        }
+    };
+    // Bring the accumulators from reference `from` to `to` (per lane).
+    auto rescale = [&](int qg, float from, float to) {
+        const float alpha = fast_exp2(from - to);
+        acc_l[qg] *= alpha;
+        if constexpr (kV) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) acc[qg][dt] *= alpha;
+        }
+    };
+    // Decide the next reference after a half with column maxima mx; if a max
+    // jumped past the fp32-safe range, rescale now and recompute that half's P.
+    auto settle = [&](auto full_c, const f32x4 (&sacc)[QG][2], const int32_t *pib, int kh, u32x4 (&pb)[QG],
+                      const float (&mx)[QG], float (&m_next)[QG], float (&cs)[16]) {
+        bool big = false;
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+            m_next[qg] = mx[qg] > m_ref[qg] + kRescaleSlack ? mx[qg] : m_ref[qg];
+            big = big || mx[qg] > m_ref[qg] + 64.f;
+        }
+        if (__any(big)) {
+            float mx2[QG];
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) {
+                rescale(qg, m_ref[qg], m_next[qg]);
+                m_ref[qg] = m_next[qg];
+            }
+            softmax_half(full_c, sacc, pib, kh, pb, mx2, cs);
+        }
+    };
+    // After a half's PV: move the accumulators to the new reference.
+    auto commit = [&](const float (&m_next)[QG]) {
+        bool moved = false;
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) moved = moved || m_next[qg] != m_ref[qg];
+        if (__any(moved)) {
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) rescale(qg, m_ref[qg], m_next[qg]);
+        }
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) m_ref[qg] = m_next[qg];
+    };
+
+    f32x4 sA[QG][2], sB[QG][2];
+    if (ntiles > 0) qk_half(Ks, 0, sA);
+
+    // One tile; MORE: a next tile exists (stage it), FULL: no masking needed.
+    // Each region is straight-line code so the MFMA / VALU interleave hints
+    // apply to it.
+    auto tile_body = [&](auto more_c, auto full_c, int it) {
+        constexpr bool MORE = decltype(more_c)::value;
         const int cur = it & 1;
         const int tile = key_begin + it * kTileN;
         const uint16_t *Kc = Ks + cur * GG::KBUF;
         const uint16_t *Vc = Vs + (kV ? cur * GG::VBUF : 0);
         const int32_t *pc_ = s_pi + cur * kTileN;
-        const bool more = it + 1 < ntiles;
-        if (more) {
+        u32x4 pb0[QG], pb1[QG];
+        float mx0[QG], mx1[QG], mn0[QG], mn1[QG];
+        float cs[16];   // kMass: column sums of this lane's 16 keys
+#pragma unroll
+        for (int u = 0; u < 16; ++u) cs[u] = 0.f;
+        if constexpr (MORE) {
             data_load<D, WAVES>(p, dnext, m2, g, tile + kTileN, tid, kV);
             if (it + 2 < ntiles) meta_load<D, WAVES>(m2, bt, pis, tile + 2 * kTileN, key_end, tid);
         }
 
-        float cs[16];   // kMass: column sums of this lane's 16 keys
-        if constexpr (MODE == kMass) {
-#pragma unroll
-            for (int u = 0; u < 16; ++u) cs[u] = 0.f;
-        }
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            if (kh == 1 && more) cs_load<D, WAVES>(p, dnext, tid);
-            // ---- S^T = K Q^T for a 32-key half: sacc[qg][T]
-            f32x4 sacc[QG][2];
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) sacc[qg][0] = sacc[qg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int T = 0; T < 2; ++T) {
-                const int key = 32 * kh + 8 * (lc >> 2) + 4 * T + (lc & 3);
-                const int sw = kswz(key);
-#pragma unroll
-                for (int c = 0; c < GG::NC; ++c) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(Kc + key * GG::KS + 8 * ((4 * c + lg) ^ sw));
-#pragma unroll
-                    for (int qg = 0; qg < QG; ++qg) sacc[qg][T] = mfma16(a, qop[qg][c], sacc[qg][T]);
-                }
-            }
-            // pi of this lane's 8 keys (only read on tiles that need masking)
-            int kp[8];
-            if (!full) {
-                const i32x4 a = *reinterpret_cast<const i32x4 *>(pc_ + 32 * kh + 8 * lg);
-                const i32x4 b = *reinterpret_cast<const i32x4 *>(pc_ + 32 * kh + 8 * lg + 4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    kp[i] = a[i];
-                    kp[4 + i] = b[i];
-                }
-            }
-            u32x4 pb[QG];
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-                float s[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) s[e] = sacc[qg][e >> 2][e & 3];
-                if (!full) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const bool vis = kp[e] >= 0 && kp[e] <= qpos[qg];
-                        s[e] = vis ? s[e] : -INFINITY;
-                    }
-                }
-                if constexpr (MODE == kMass) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) cs[kh * 8 + e] += fast_exp2(fmaf(s[e], sc, -lse2[qg]));
-                } else {
-                    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                                     fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-                    mx = col_max(mx);
-                    const float mxs = mx * sc;
-                    const bool need = mxs > m_run[qg] + kRescaleSlack;
-                    if (__any(need)) {
-                        const float m_new = need ? mxs : m_run[qg];
-                        const float alpha = need ? fast_exp2(m_run[qg] - m_new) : 1.f;
-                        m_run[qg] = m_new;
-                        acc_l[qg] *= alpha;
-                        if constexpr (kV) {
-#pragma unroll
-                            for (int dt = 0; dt < D / 16; ++dt) acc[qg][dt] *= alpha;
-                        }
-                    }
-                    const float mu = m_run[qg];
-                    u32x4 pq;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        pq[e] = pack2(fast_exp2(fmaf(s[2 * e], sc, -mu)), fast_exp2(fmaf(s[2 * e + 1], sc, -mu)));
-                    pb[qg] = pq;
-                }
-            }
-            if constexpr (MODE != kMass) {
-#pragma unroll
-                for (int qg = 0; qg < QG; ++qg) acc_l[qg] = mfma16(ones_a, pb[qg], acc_l[qg]);
-            }
-            if constexpr (kV) {
-                // ---- O^T += V^T P^T: one V operand feeds every column group
-#pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(Vc + (16 * dt + lc) * GG::VS + 32 * kh + 8 * lg);
-#pragma unroll
-                    for (int qg = 0; qg < QG; ++qg) acc[qg][dt] = mfma16(a, pb[qg], acc[qg][dt]);
-                }
-            }
+        // R1: QK(half 1) || softmax(half 0)
+        qk_half(Kc, 1, sB);
+        softmax_half(full_c, sA, pc_, 0, pb0, mx0, cs);
+        interleave_hint<2 * QG * GG::NC, 4>();
+        if constexpr (MODE != kMass) settle(full_c, sA, pc_, 0, pb0, mx0, mn0, cs);
+
+        // R2: PV(half 0) || softmax(half 1)
+        pv_half(Vc, 0, pb0);
+        if constexpr (MORE) cs_load<D, WAVES>(p, dnext, tid);
+        softmax_half(full_c, sB, pc_, 1, pb1, mx1, cs);
+        if constexpr (MODE != kMass) {
+            interleave_hint<QG * (D / 16 + 1), 4>();
+            commit(mn0);
+            settle(full_c, sB, pc_, 1, pb1, mx1, mn1, cs);
         }
 
+        // R3: PV(half 1) || rotate + stage the next tile
+        pv_half(Vc, 1, pb1);
         if constexpr (MODE == kMass) {
             // Sum the 16 columns of the lane group: butterfly reduce-scatter,
             // afterwards lane lc holds the total of value index u = lc.
@@ -509,13 +606,16 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
             const int key = 32 * (lc >> 3) + 8 * lg + 4 * ((lc >> 2) & 1) + (lc & 3);
             s_red[(cur * WAVES + wave) * kTileN + key] = cs[0];
         }
-
-        // ---- stage the next tile into the other buffer
         bool f = true;
-        if (more)
+        if constexpr (MORE)
             f = data_store<D, WAVES>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs + (kV ? (cur ^ 1) * GG::VBUF : 0),
                                      s_pi + (cur ^ 1) * kTileN, tid, kV, min_pos);
-        full = __syncthreads_and(f);
+        if constexpr (MODE != kMass) {
+            interleave_hint<QG * (D / 16 + 1), 3>();
+            commit(mn1);
+        }
+        (void)f;
+        __syncthreads();
 
         if constexpr (MODE == kMass) {
             if (tid < kTileN) {
@@ -528,7 +628,28 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
                     p.mass_part[(((size_t)r * p.hkv + g) * p.row_blocks + rb) * p.mass_stride + j] = tot;
             }
         }
+        // R4: QK(next tile, half 0)
+        if constexpr (MORE) qk_half(Ks + (cur ^ 1) * GG::KBUF, 0, sA);
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    // One loop per workgroup kind, so that each keeps its own register
+    // allocation: every key of the range usable and visible to every row ->
+    // mask-free tiles; otherwise every tile masked.  A partial last tile is
+    // always masked.
+    const bool last_partial = ntiles > 0 && key_end - (key_begin + (ntiles - 1) * kTileN) < kTileN;
+    if (wg_full) {
+        for (int it = 0; it + 1 < ntiles; ++it) tile_body(T_{}, T_{}, it);
+        if (ntiles > 0) {
+            if (last_partial) tile_body(F_{}, F_{}, ntiles - 1);
+            else tile_body(F_{}, T_{}, ntiles - 1);
+        }
+    } else {
+        for (int it = 0; it + 1 < ntiles; ++it) tile_body(T_{}, F_{}, it);
+        if (ntiles > 0) tile_body(F_{}, F_{}, ntiles - 1);
     }
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) m_run[qg] = m_ref[qg];
     if constexpr (MODE == kMass) return;
 
     // ---- epilogue: per-lane partial sums -> column totals
