@@ -135,23 +135,46 @@ struct Geo {
     static constexpr int PC = D / 16;            // 8-pair chunks per key
     static constexpr int KTASK = kTileN * PC / NT;   // K staging tasks per thread
     static constexpr int VCH = 8 * D / NT;       // V 16-byte chunks per thread
-    static constexpr int KS = D + 8;             // LDS row stride of K (bf16), padded 16 B
-    static constexpr int VS = kTileN + 8;        // LDS row stride of V^T (bf16), padded
-    static constexpr int KBUF = kTileN * KS;     // one K buffer (bf16 elements)
-    static constexpr int VBUF = D * VS;          // one V^T buffer
+    static constexpr int KBUF = kTileN * D;      // one K tile (bf16 elements), chunk-major
+    static constexpr int VBUF = D * kTileN;      // one V^T tile, chunk-major
     static_assert(KTASK >= 1 && VCH >= 1, "staging needs at least one task per thread");
 };
 
 // K tile key k = 32*kh + 8*a + 4*T + b lives in LDS row
 // krow(k) = 32*kh + 16*T + 4*a + b: the 16 keys that one MFMA operand read
-// takes (MFMA row m = 4a + b of tile T) are 16 consecutive rows, which the
-// 16-byte row padding spreads over all bank groups (conflict-free); the read
-// address is one per-lane base plus immediates.
+// takes (MFMA row m = 4a + b of tile T) are 16 consecutive rows.
 __device__ __forceinline__ int krow(int k) {
     return (k & ~31) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
 }
 
-// Block ids / positions of one tile for this thread's staging tasks.
+// LDS tile layouts (gfx950 measured: a ds_read_b128 is conflict-free when
+// each 16 consecutive lanes read one aligned 256-byte block in any
+// XOR-permuted order; a ds_write_b128 when each 8 consecutive lanes write one
+// aligned 128-byte block).  Both tiles are chunk-major: the 16-byte chunks of
+// 64 consecutive rows form one 1 KB run, with the row index XOR-ed in its low
+// three bits by a function of the chunk.
+//  K tile, rows = keys (krow order), chunk ch = elements 8ch..8ch+7 of d.
+//  The XOR spreads one key's PC chunks (one 8-lane write group) over the
+//  eight 16-byte slots of a 128-byte block.
+template <int D>
+__device__ __forceinline__ int kxor(int ch) { return (ch % (D / 16)) * (8 / (D / 16)); }
+template <int D>
+__device__ __forceinline__ int koff(int r, int ch) { return ch * (kTileN * 8) + ((r ^ kxor<D>(ch)) * 8); }
+//  V^T tile, rows = d, chunk ch = keys 8ch..8ch+7; rows in 64-row halves.
+__device__ __forceinline__ int voff(int d, int ch) {
+    return (d >> 6) * (64 * kTileN) + ch * (64 * 8) + (((d & 63) ^ (ch & 7)) * 8);
+}
+// V staging lane map: each 8 consecutive lanes take 8 consecutive d rows of
+// one 8-key chunk (one 128-byte LDS block per write group).
+__device__ __forceinline__ void vmap(int tid, int &half, int &dd) {
+    const int l = tid & 63;
+    half = (l >> 3) & 1;
+    dd = (l & 7) | ((l >> 4) << 3);
+}
+
+// Block ids / positions of one tile for this thread's staging tasks, as
+// loaded (at clamped indices); the range check is applied where they are used,
+// one tile later, so that no wait for these loads sits at the tile start.
 template <int D, int WAVES>
 struct Meta {
     int32_t kblk[Geo<D, WAVES>::KTASK], kpi[Geo<D, WAVES>::KTASK];
@@ -179,25 +202,19 @@ __device__ __forceinline__ void meta_load(Meta<D, WAVES> &m, const int32_t *bt, 
     const int last = key_end - 1;   // callers only load tiles with tile < key_end
 #pragma unroll
     for (int u = 0; u < GG::KTASK; ++u) {
-        const int j = tile + tid / GG::PC + u * (GG::NT / GG::PC);
-        const int jc = min(j, last);
-        const int b = bt[jc >> 4], pi = pis[jc];
-        m.kblk[u] = j <= last ? b : -1;
-        m.kpi[u] = j <= last ? pi : -1;
+        const int jc = min(tile + tid / GG::PC + u * (GG::NT / GG::PC), last);
+        m.kblk[u] = bt[jc >> 4];
+        m.kpi[u] = pis[jc];
     }
     // V staging: every lane of this wave covers keys of tile block (wave & 3)
-    const int bq = (tid >> 6) & 3;
-    const int jb = tile + 16 * bq;
-    const int b0 = bt[min(jb, last) >> 4];
-    m.vblk = jb <= last ? b0 : -1;
-    const int jl = jb + (tid & 15);
-    const int pl = pis[min(jl, last)];
-    m.vkey_pi = jl <= last ? pl : -1;
+    const int jb = tile + 16 * ((tid >> 6) & 3);
+    m.vblk = bt[min(jb, last) >> 4];
+    m.vkey_pi = pis[min(jb + (tid & 15), last)];
 }
 
 template <int D, int WAVES>
 __device__ __forceinline__ void data_load(const FwdParams &p, Data<D, WAVES> &dt, const Meta<D, WAVES> &m, int g,
-                                          int tile, int tid, bool need_v) {
+                                          int tile, int key_end, int tid, bool need_v) {
     using GG = Geo<D, WAVES>;
 #pragma unroll
     for (int u = 0; u < GG::KTASK; ++u) {
@@ -205,7 +222,7 @@ __device__ __forceinline__ void data_load(const FwdParams &p, Data<D, WAVES> &dt
         const int pc = tid % GG::PC;
         const int j = tile + kk;
         const int blk = m.kblk[u], pi = m.kpi[u];
-        const bool ok = blk >= 0 && blk < p.num_blocks && pi >= 0 && pi < p.max_pos;
+        const bool ok = j < key_end && (unsigned)blk < (unsigned)p.num_blocks && (unsigned)pi < (unsigned)p.max_pos;
         dt.kpi[u] = ok ? pi : -1;
         // unusable keys read the zero page: no branch, and they rotate to zero
         const uint16_t *row = ok ? p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + (j & 15)) * D : p.zero_page;
@@ -213,11 +230,13 @@ __device__ __forceinline__ void data_load(const FwdParams &p, Data<D, WAVES> &dt
         dt.khi[u] = *reinterpret_cast<const u32x4 *>(row + GG::HALF + 8 * pc);
     }
     if (!need_v) return;
-    const int half = tid & 1, dd = (tid >> 1) & 31;
-    const bool bok = m.vblk >= 0 && m.vblk < p.num_blocks;
+    int half, dd;
+    vmap(tid, half, dd);
+    const int jb = tile + 16 * ((tid >> 6) & 3);
+    const bool bok = jb < key_end && (unsigned)m.vblk < (unsigned)p.num_blocks;
     // validity of the block's 16 keys: lanes 0..15 hold their pi; the ballot
     // lands in scalar registers
-    const bool kv_ok = m.vkey_pi >= 0 && m.vkey_pi < p.max_pos;
+    const bool kv_ok = jb + (tid & 15) < key_end && (unsigned)m.vkey_pi < (unsigned)p.max_pos;
     const uint32_t okmask = (uint32_t)__ballot(kv_ok) & 0xffffu;
     dt.vmask = bok ? (int32_t)((~okmask >> (8 * half)) & 0xffu) : 0xff;
     const int32_t vm = dt.vmask;
@@ -261,28 +280,34 @@ __device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uin
         u32x4 lo = dt.klo[u], hi = dt.khi[u];
         rope8(lo, hi, dt.cs[u][0], dt.cs[u][1], dt.cs[u][2], dt.cs[u][3]);
         const int kr = krow(kk);
-        *reinterpret_cast<u32x4 *>(Ks + kr * GG::KS + 8 * pc) = lo;
-        *reinterpret_cast<u32x4 *>(Ks + kr * GG::KS + GG::HALF + 8 * pc) = hi;
+        *reinterpret_cast<u32x4 *>(Ks + koff<D>(kr, pc)) = lo;
+        *reinterpret_cast<u32x4 *>(Ks + koff<D>(kr, GG::PC + pc)) = hi;
         // masked-path visibility is one compare: unusable keys get INT_MAX
         if (pc == 0) s_pi[kk] = pi >= 0 ? pi : 0x7fffffff;
         full = full && pi >= 0 && pi <= min_pos;
     }
     if (need_v) {
-        const int half = tid & 1, dd = (tid >> 1) & 31, b = (tid >> 6) & 3;
+        int half, dd;
+        vmap(tid, half, dd);
+        const int b = (tid >> 6) & 3;
         const int vm = dt.vmask;
-        // keep masks: unusable keys are zeroed so that 0 * garbage cannot
-        // poison O (branch-free: the staging sits inside an MFMA region)
-        uint32_t keep[4];
+        // unusable keys are zeroed so that 0 * garbage cannot poison O; the
+        // masks are only built when some chunk of the wave needs them
+        if (__any(vm != 0)) {
+            uint32_t keep[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            keep[e] = ((vm >> (2 * e)) & 1 ? 0u : 0x0000ffffu) | ((vm >> (2 * e + 1)) & 1 ? 0u : 0xffff0000u);
+            for (int e = 0; e < 4; ++e)
+                keep[e] = ((vm >> (2 * e)) & 1 ? 0u : 0x0000ffffu) | ((vm >> (2 * e + 1)) & 1 ? 0u : 0xffff0000u);
+#pragma unroll
+            for (int u = 0; u < GG::VCH; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dt.v[u][e] &= keep[e];
+        }
 #pragma unroll
         for (int u = 0; u < GG::VCH; ++u) {
-            u32x4 v = dt.v[u];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] &= keep[e];
+            const u32x4 v = dt.v[u];
             const int d = dd + 32 * ((tid >> 8) + u * (GG::NT / 256));
-            *reinterpret_cast<u32x4 *>(Vs + d * GG::VS + 16 * b + 8 * half) = v;
+            *reinterpret_cast<u32x4 *>(Vs + voff(d, 2 * b + half)) = v;
         }
     }
     return full;
@@ -297,7 +322,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t Vs[kV ? 2 * GG::VBUF : 8];
     __shared__ __attribute__((aligned(16))) int32_t s_pi[2 * kTileN];
     __shared__ float s_red[MODE == kMass ? 2 * WAVES * kTileN : 1];
-    __shared__ int32_t s_minpos;
+    __shared__ int32_t s_minpos, s_firstbad;
 
     const int nwg = p.row_blocks * p.hkv * p.num_splits * p.batch;
     int lid = xcd_remap(blockIdx.x, nwg);
@@ -324,7 +349,10 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int lc = lane & 15, lg = lane >> 4;
-    if (tid == 0) s_minpos = 0x7fffffff;
+    if (tid == 0) {
+        s_minpos = 0x7fffffff;
+        s_firstbad = 0x7fffffff;
+    }
 
     // ---- this lane's query columns: load, rotate at q_pos, keep as B operands
     u32x4 qop[QG][GG::NC];
@@ -396,28 +424,30 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
     Meta<D, WAVES> m1, m2;
     Data<D, WAVES> dnext;
-    bool full = false;
     if (ntiles > 0) {
         meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end, tid);
         if (ntiles > 1) meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
-        data_load<D, WAVES>(p, dnext, m1, g, key_begin, tid, kV);
+        data_load<D, WAVES>(p, dnext, m1, g, key_begin, key_end, tid, kV);
         cs_load<D, WAVES>(p, dnext, tid);
     }
     __syncthreads();
     const int min_pos = s_minpos;
-    // Is every key of this workgroup's range usable and visible to all of
-    // its rows?  (pi and block ids are small and L2-resident.)
-    bool my_ok = true;
+    // First key of this workgroup's range that is unusable or not visible to
+    // every row (pi and block ids are small and L2-resident): tiles before it
+    // need no mask.
     for (int j = key_begin + tid; j < key_end; j += GG::NT) {
         const int pi = pis[j], blk = bt[j >> 4];
-        my_ok = my_ok && pi >= 0 && pi < p.max_pos && pi <= min_pos && blk >= 0 && blk < p.num_blocks;
+        if (!(pi >= 0 && pi < p.max_pos && pi <= min_pos && blk >= 0 && blk < p.num_blocks)) {
+            atomicMin(&s_firstbad, j);
+            break;
+        }
     }
-    const bool wg_full = __syncthreads_and(my_ok);
+    __syncthreads();
+    const int first_bad = s_firstbad;
     if (ntiles > 0) {
-        const bool f = data_store<D, WAVES>(dnext, Ks, Vs, s_pi, tid, kV, min_pos);
-        full = __syncthreads_and(f);
+        (void)data_store<D, WAVES>(dnext, Ks, Vs, s_pi, tid, kV, min_pos);
+        __syncthreads();
     }
-    (void)full;
     const float sc = p.scale_log2;
     float m_ref[QG];                    // reference max of the next P half
 #pragma unroll
@@ -440,12 +470,14 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         for (int qg = 0; qg < QG; ++qg) sacc[qg][0] = sacc[qg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         // d-chunk outermost: 2*QG independent accumulators separate the
         // dependent MFMAs of one accumulator chain
-        const uint16_t *k0 = Kb + (32 * kh + lc) * GG::KS + 8 * lg;   // krow of tile T = 0 keys
-        const uint16_t *k1 = k0 + 16 * GG::KS;                          // tile T = 1
+        // rows 32*kh + 16*T + lc (T = 0, 1), chunk 4c + lg: the XOR stays
+        // inside lc, so the row offset is an immediate
 #pragma unroll
         for (int c = 0; c < GG::NC; ++c) {
-            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(k0 + 32 * c);
-            const u32x4 a1 = *reinterpret_cast<const u32x4 *>(k1 + 32 * c);
+            const int ch = 4 * c + lg;
+            const uint16_t *k0 = Kb + ch * (kTileN * 8) + ((lc ^ kxor<D>(ch)) * 8) + (32 * kh) * 8;
+            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(k0);
+            const u32x4 a1 = *reinterpret_cast<const u32x4 *>(k0 + 16 * 8);
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) {
                 sacc[qg][0] = mfma16(a0, qop[qg][c], sacc[qg][0]);
@@ -487,9 +519,9 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
                 for (int e = 0; e < 4; ++e)
                     pq[e] = pack2(fast_exp2(fmaf(s[2 * e], sc, -mu)), fast_exp2(fmaf(s[2 * e + 1], sc, -mu)));
                 pb[qg] = pq;
-                const float m8 = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                                       fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-                mx[qg] = col_max(m8) * sc;
+                // lane-local maximum of the raw scores; the column maximum
+                // is only formed when some lane passes the reference
+                mx[qg] = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
             }
         }
     };
@@ -501,7 +533,9 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         if constexpr (kV) {
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(Vb + (16 * dt + lc) * GG::VS + 32 * kh + 8 * lg);
+                const int ch = 4 * kh + lg;
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(
+                    Vb + (dt >> 2) * (64 * kTileN) + ch * (64 * 8) + (lc ^ ch) * 8 + (dt & 3) * 16 * 8);
 #pragma unroll
                 for (int qg = 0; qg < QG; ++qg) acc[qg][dt] = mfma16(a, pb[qg], acc[qg][dt]);
             }
@@ -516,24 +550,35 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
             for (int dt = 0; dt < D / 16; ++dt) acc[qg][dt] *= alpha;
         }
     };
-    // Decide the next reference after a half with column maxima mx; if a max
-    // jumped past the fp32-safe range, rescale now and recompute that half's P.
+    // Decide the next reference after a half whose lane-local raw maxima are
+    // mx.  Only when some lane passed the reference by more than the slack are
+    // the column maxima formed (wave-uniform branch); if one jumped past the
+    // fp32-safe range, rescale now and recompute that half's P.
     auto settle = [&](auto full_c, const f32x4 (&sacc)[QG][2], const int32_t *pib, int kh, u32x4 (&pb)[QG],
                       const float (&mx)[QG], float (&m_next)[QG], float (&cs)[16]) {
-        bool big = false;
+        bool need = false;
 #pragma unroll
         for (int qg = 0; qg < QG; ++qg) {
-            m_next[qg] = mx[qg] > m_ref[qg] + kRescaleSlack ? mx[qg] : m_ref[qg];
-            big = big || mx[qg] > m_ref[qg] + 64.f;
+            m_next[qg] = m_ref[qg];
+            need = need || mx[qg] * sc > m_ref[qg] + kRescaleSlack;
         }
-        if (__any(big)) {
-            float mx2[QG];
+        if (__any(need)) {
+            bool big = false;
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) {
-                rescale(qg, m_ref[qg], m_next[qg]);
-                m_ref[qg] = m_next[qg];
+                const float cm = col_max(mx[qg]) * sc;
+                m_next[qg] = cm > m_ref[qg] + kRescaleSlack ? cm : m_ref[qg];
+                big = big || cm > m_ref[qg] + 64.f;
             }
-            softmax_half(full_c, sacc, pib, kh, pb, mx2, cs);
+            if (__any(big)) {
+                float mx2[QG];
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg) {
+                    rescale(qg, m_ref[qg], m_next[qg]);
+                    m_ref[qg] = m_next[qg];
+                }
+                softmax_half(full_c, sacc, pib, kh, pb, mx2, cs);
+            }
         }
     };
     // After a half's PV: move the accumulators to the new reference.
@@ -568,7 +613,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) cs[u] = 0.f;
         if constexpr (MORE) {
-            data_load<D, WAVES>(p, dnext, m2, g, tile + kTileN, tid, kV);
+            data_load<D, WAVES>(p, dnext, m2, g, tile + kTileN, key_end, tid, kV);
             if (it + 2 < ntiles) meta_load<D, WAVES>(m2, bt, pis, tile + 2 * kTileN, key_end, tid);
         }
 
@@ -633,20 +678,18 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
-    // One loop per workgroup kind, so that each keeps its own register
-    // allocation: every key of the range usable and visible to every row ->
-    // mask-free tiles; otherwise every tile masked.  A partial last tile is
-    // always masked.
+    // Tiles before the one holding the first unusable / not-yet-visible key
+    // run mask-free, the rest masked; each loop keeps its own register
+    // allocation.  A partial last tile is always masked.
+    const int t_split = first_bad == 0x7fffffff ? ntiles : (first_bad - key_begin) / kTileN;
     const bool last_partial = ntiles > 0 && key_end - (key_begin + (ntiles - 1) * kTileN) < kTileN;
-    if (wg_full) {
-        for (int it = 0; it + 1 < ntiles; ++it) tile_body(T_{}, T_{}, it);
-        if (ntiles > 0) {
-            if (last_partial) tile_body(F_{}, F_{}, ntiles - 1);
-            else tile_body(F_{}, T_{}, ntiles - 1);
-        }
-    } else {
-        for (int it = 0; it + 1 < ntiles; ++it) tile_body(T_{}, F_{}, it);
-        if (ntiles > 0) tile_body(F_{}, F_{}, ntiles - 1);
+    const int nf = min(t_split, ntiles - 1);
+    int it = 0;
+    for (; it < nf; ++it) tile_body(T_{}, T_{}, it);
+    for (; it < ntiles - 1; ++it) tile_body(T_{}, F_{}, it);
+    if (ntiles > 0) {
+        if (t_split >= ntiles && !last_partial) tile_body(F_{}, T_{}, ntiles - 1);
+        else tile_body(F_{}, F_{}, ntiles - 1);
     }
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) m_run[qg] = m_ref[qg];
