@@ -199,7 +199,7 @@ template <int D, int WAVES>
 __device__ __forceinline__ void meta_load(Meta<D, WAVES> &m, const int32_t *bt, const int32_t *pis, int tile,
                                           int key_end, int tid) {
     using GG = Geo<D, WAVES>;
-    const int last = key_end - 1;   // callers only load tiles with tile < key_end
+    const int last = key_end - 1;   // key_end >= 1; tiles past the range clamp to the last key
 #pragma unroll
     for (int u = 0; u < GG::KTASK; ++u) {
         const int jc = min(tile + tid / GG::PC + u * (GG::NT / GG::PC), last);
@@ -422,11 +422,15 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     __syncthreads();
     atomicMin(&s_minpos, my_min);
     const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
+    // Staging pipeline: the data of tile t+2 (and the block ids of t+3) are
+    // requested next to the QK of tile t+1, about a tile before they are
+    // rotated and stored; indices past the range are clamped and such keys
+    // read the zero page, so the requests need no branch.
     Meta<D, WAVES> m1, m2;
     Data<D, WAVES> dnext;
     if (ntiles > 0) {
         meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end, tid);
-        if (ntiles > 1) meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
+        meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
         data_load<D, WAVES>(p, dnext, m1, g, key_begin, key_end, tid, kV);
         cs_load<D, WAVES>(p, dnext, tid);
     }
@@ -595,7 +599,11 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     };
 
     f32x4 sA[QG][2], sB[QG][2];
-    if (ntiles > 0) qk_half(Ks, 0, sA);
+    if (ntiles > 0) {
+        qk_half(Ks, 0, sA);
+        data_load<D, WAVES>(p, dnext, m2, g, key_begin + kTileN, key_end, tid, kV);
+        meta_load<D, WAVES>(m2, bt, pis, key_begin + 2 * kTileN, key_end, tid);
+    }
 
     // One tile; MORE: a next tile exists (stage it), FULL: no masking needed.
     // Each region is straight-line code so the MFMA / VALU interleave hints
@@ -612,10 +620,6 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         float cs[16];   // kMass: column sums of this lane's 16 keys
 #pragma unroll
         for (int u = 0; u < 16; ++u) cs[u] = 0.f;
-        if constexpr (MORE) {
-            data_load<D, WAVES>(p, dnext, m2, g, tile + kTileN, key_end, tid, kV);
-            if (it + 2 < ntiles) meta_load<D, WAVES>(m2, bt, pis, tile + 2 * kTileN, key_end, tid);
-        }
 
         // R1: QK(half 1) || softmax(half 0)
         qk_half(Kc, 1, sB);
@@ -673,8 +677,12 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
                     p.mass_part[(((size_t)r * p.hkv + g) * p.row_blocks + rb) * p.mass_stride + j] = tot;
             }
         }
-        // R4: QK(next tile, half 0)
-        if constexpr (MORE) qk_half(Ks + (cur ^ 1) * GG::KBUF, 0, sA);
+        // R4: QK(next tile, half 0) || request tile t+2
+        if constexpr (MORE) {
+            qk_half(Ks + (cur ^ 1) * GG::KBUF, 0, sA);
+            data_load<D, WAVES>(p, dnext, m2, g, tile + 2 * kTileN, key_end, tid, kV);
+            meta_load<D, WAVES>(m2, bt, pis, tile + 3 * kTileN, key_end, tid);
+        }
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
