@@ -75,8 +75,24 @@ FwdPlan plan_fwd(const pic_config &c, int batch, int max_q_len, int max_kv_len) 
     return pl;
 }
 
-int decode_splits(int max_kv_len) {
-    return max_kv_len > 0 ? (max_kv_len + pic::kDecodeSplit - 1) / pic::kDecodeSplit : 1;
+// Decode: about four 256-thread workgroups per CU in total, each covering
+// split_len keys (a multiple of 4 waves x 32 keys, at least 512) of one
+// (request, kv head).
+struct DecodePlan {
+    int split_len = 512;
+    int num_splits = 1;
+};
+
+DecodePlan plan_decode(int batch, int hkv, int max_kv_len) {
+    DecodePlan d;
+    if (max_kv_len <= 0 || batch <= 0) return d;
+    const long long rows = (long long)batch * hkv;
+    const long long per = (rows * max_kv_len + 4LL * kCUs - 1) / (4LL * kCUs);
+    long long len = (per + 127) / 128 * 128;
+    len = std::max(512LL, std::min(len, ((long long)max_kv_len + 127) / 128 * 128));
+    d.split_len = (int)len;
+    d.num_splits = (int)((max_kv_len + len - 1) / len);
+    return d;
 }
 
 // Workspace layouts (byte offsets, 256-aligned).
@@ -267,7 +283,7 @@ pic_status pic_workspace_bytes(const pic_ctx *ctx, pic_op op, const pic_req_tabl
         return PIC_OK;
     }
     case PIC_OP_DECODE:
-        *bytes = decode_ws(c, req->batch, decode_splits(req->max_kv_len)).total;
+        *bytes = decode_ws(c, req->batch, plan_decode(req->batch, c.num_kv_heads, req->max_kv_len).num_splits).total;
         return PIC_OK;
     case PIC_OP_SELECT: {
         if (total_q < 0 || max_q_len < 0) return PIC_ERR_INVALID_ARG;
@@ -339,7 +355,8 @@ pic_status pic_attn_decode(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
     if (c.num_q_heads / c.num_kv_heads > 16)
         return fail(ctx, PIC_ERR_UNSUPPORTED, "decode supports up to 16 q heads per kv head%s");
     if (req->batch == 0) return PIC_OK;
-    const int splits = decode_splits(req->max_kv_len);
+    const DecodePlan dp = plan_decode(req->batch, c.num_kv_heads, req->max_kv_len);
+    const int splits = dp.num_splits;
     const DecodeWs w = decode_ws(c, req->batch, splits);
     if (w.total > 0 && (!ws || ws_bytes < w.total))
         return fail(ctx, PIC_ERR_WORKSPACE, "workspace too small for decode%s");
@@ -365,6 +382,7 @@ pic_status pic_attn_decode(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
     p.max_pos = c.max_position;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
     p.max_kv_len = req->max_kv_len;
+    p.split_len = dp.split_len;
     p.num_splits = splits;
     p.out = out;
     p.lse = lse;

@@ -4,14 +4,22 @@
 //
 // Bound by HBM bytes: every cached key and value is read once per
 // (request, kv head) and feeds only G = Hq/Hkv query rows.  So there is no
-// LDS staging: each wave streams its own 32-key steps straight from global
-// memory into MFMA operand registers, rotates the K operand in registers with
-// the fp32 cos/sin row of the key's pi, and runs the same transposed
-// S^T = K Q^T / O^T += V^T P^T scheme as the prefill kernel (the G query heads
-// are the MFMA columns; columns >= G are masked).  The next step's loads are
-// issued before the current step's math.  A workgroup (4 waves) covers 1024
-// keys of one (request, kv head); waves are merged through LDS and splits by
-// the LSE merge kernel.
+// LDS staging of K/V: each wave streams its own 32-key steps straight from
+// global memory into MFMA operand registers (the next step's K, V and
+// positions are requested before the current step's math), rotates the K
+// operand in registers, and runs the same transposed S^T = K Q^T /
+// O^T += V^T P^T scheme as the prefill kernel (the G query heads are the MFMA
+// columns; columns >= G are masked).
+//
+// Rotation of key j at position pi uses R(pi) = R(pi - dl) R(dl) with dl the
+// key's offset inside its 16-key block (capped at pi): the keys of a block
+// that holds consecutive positions then all read the one table row pi - dl,
+// which stays in L1, and R(dl) for dl = 0..15 (rows 0..15 of the same table)
+// sits in LDS.  Any dl in 0..pi gives the same rotation, so blocks holding
+// arbitrary positions are handled by the same code.
+//
+// A workgroup (4 waves) covers split_len keys of one (request, kv head);
+// waves are merged through LDS and splits by the LSE merge kernel.
 #include "pic_internal.h"
 
 namespace pic {
@@ -35,21 +43,18 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ void rope8(u32x4 &lo, u32x4 &hi, const f32x4 c0, const f32x4 c1,
-                                      const f32x4 s0, const f32x4 s1) {
-    const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-    const float s[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    u32x4 ro, rh;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float a0 = bf_lo(lo[e]), a1 = bf_hi(lo[e]);
-        const float b0 = bf_lo(hi[e]), b1 = bf_hi(hi[e]);
-        const float cc0 = c[2 * e], cc1 = c[2 * e + 1], ss0 = s[2 * e], ss1 = s[2 * e + 1];
-        ro[e] = pack2(fmaf(a0, cc0, -b0 * ss0), fmaf(a1, cc1, -b1 * ss1));
-        rh[e] = pack2(fmaf(a0, ss0, b0 * cc0), fmaf(a1, ss1, b1 * cc1));
-    }
-    lo = ro;
-    hi = rh;
+// Rotate 4 RoPE pairs: words 2*hh, 2*hh+1 of lo hold x[i..i+3] (first
+// halves, two bf16 per word), the same words of hi the second halves x[i+d/2..];
+// c/s the cos/sin of the 4 pairs.  Result rounded to bf16.
+template <int hh>
+__device__ __forceinline__ void rope4(u32x4 &lo, u32x4 &hi, const f32x4 c, const f32x4 s) {
+    const uint32_t l0 = lo[2 * hh], l1 = lo[2 * hh + 1], h0 = hi[2 * hh], h1 = hi[2 * hh + 1];
+    const float a0 = bf_lo(l0), a1 = bf_hi(l0), a2 = bf_lo(l1), a3 = bf_hi(l1);
+    const float b0 = bf_lo(h0), b1 = bf_hi(h0), b2 = bf_lo(h1), b3 = bf_hi(h1);
+    lo[2 * hh] = pack2(fmaf(a0, c[0], -b0 * s[0]), fmaf(a1, c[1], -b1 * s[1]));
+    lo[2 * hh + 1] = pack2(fmaf(a2, c[2], -b2 * s[2]), fmaf(a3, c[3], -b3 * s[3]));
+    hi[2 * hh] = pack2(fmaf(a0, s[0], b0 * c[0]), fmaf(a1, s[1], b1 * c[1]));
+    hi[2 * hh + 1] = pack2(fmaf(a2, s[2], b2 * c[2]), fmaf(a3, s[3], b3 * c[3]));
 }
 
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
@@ -59,78 +64,57 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
     return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
 }
 
-// One 32-key step's operands for one lane.
+// One 32-key step's operands for one lane (cos/sin are fetched at use).
 template <int D>
 struct Step {
     static constexpr int NC = D / 32;
-    u32x4 k[2][NC];          // A operand rows (before rotation), tiles T = 0, 1
-    f32x4 cs[2][NC / 2][4];  // cos0, cos1, sin0, sin1 for the rotated pairs
-    int32_t kpi[2];          // pi of the A row keys (-1 unusable)
-    u32x4 v[D / 16];         // V^T operand, channel 16*dt + lc, keys 8lg..8lg+7
-    int32_t spi[8];          // pi of this lane's 8 score keys (-1 unusable)
+    u32x4 k[2][NC];      // A operand rows (before rotation), tiles T = 0, 1
+    int32_t kpi[2];      // pi of the A row keys (-1 unusable)
+    u32x4 v[D / 16];     // V^T operand, channel 16*dt + lc, keys 8lg..8lg+7
+    int32_t spi[8];      // pi of this lane's 8 score keys (-1 unusable)
 };
 
+// Unconditional loads at clamped indices (key_end >= 1; kv_stride, a multiple
+// of 16, bounds every index), then selects: unusable keys read the zero page.
 template <int D>
 __device__ __forceinline__ void step_load(const DecodeParams &p, Step<D> &st, const int32_t *bt,
-                                          const int32_t *pis, int g, int kb, int key_end, int lc,
-                                          int lg) {
-    constexpr int NC = D / 32, HALF = D / 2;
+                                          const int32_t *pis, int g, int kb, int key_end, int lc, int lg) {
+    constexpr int NC = D / 32;
+    const int last = key_end - 1;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
         const int j = kb + 8 * (lc >> 2) + 4 * T + (lc & 3);
-        int pi = -1, blk = -1;
-        if (j < key_end) {
-            blk = bt[j >> 4];
-            pi = pis[j];
-        }
-        const bool ok = blk >= 0 && blk < p.num_blocks && pi >= 0 && pi < p.max_pos;
+        const int jc = min(j, last);
+        const int blk = bt[jc >> 4], pi = pis[jc];
+        const bool ok = j < key_end && (unsigned)blk < (unsigned)p.num_blocks && (unsigned)pi < (unsigned)p.max_pos;
         st.kpi[T] = ok ? pi : -1;
-        const uint16_t *row = p.k_pool + (((size_t)(ok ? blk : 0) * p.hkv + g) * kBlock + (j & 15)) * D;
-        const float *cr = p.cos_tab + (size_t)(ok ? pi : 0) * HALF;
-        const float *sr = p.sin_tab + (size_t)(ok ? pi : 0) * HALF;
+        const uint16_t *row = ok ? p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + (j & 15)) * D : p.zero_page;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-            st.k[T][c] = ok ? *reinterpret_cast<const u32x4 *>(row + 32 * c + 8 * lg) : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < NC / 2; ++c) {
-            const int i0 = 32 * c + 8 * lg;
-            st.cs[T][c][0] = *reinterpret_cast<const f32x4 *>(cr + i0);
-            st.cs[T][c][1] = *reinterpret_cast<const f32x4 *>(cr + i0 + 4);
-            st.cs[T][c][2] = *reinterpret_cast<const f32x4 *>(sr + i0);
-            st.cs[T][c][3] = *reinterpret_cast<const f32x4 *>(sr + i0 + 4);
-        }
+        for (int c = 0; c < NC; ++c) st.k[T][c] = *reinterpret_cast<const u32x4 *>(row + 32 * c + 8 * lg);
     }
-    const int j0 = kb + 8 * lg;
-    int blk = -1;
-    if (j0 < key_end) blk = bt[j0 >> 4];
-    const bool bok = blk >= 0 && blk < p.num_blocks;
-    bool all = bok && j0 + 8 <= key_end;
-    if (all) {
-        const i32x4 a = *reinterpret_cast<const i32x4 *>(pis + j0);
-        const i32x4 b = *reinterpret_cast<const i32x4 *>(pis + j0 + 4);
+    const int j0 = kb + 8 * lg;                 // multiple of 8
+    const int j0c = min(j0, last & ~7);         // 8 positions from here stay inside the row
+    const int blk = bt[j0c >> 4];
+    const bool bok = j0 < key_end && (unsigned)blk < (unsigned)p.num_blocks;
+    const i32x4 a = *reinterpret_cast<const i32x4 *>(pis + j0c);
+    const i32x4 b = *reinterpret_cast<const i32x4 *>(pis + j0c + 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            st.spi[i] = a[i];
-            st.spi[4 + i] = b[i];
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.spi[e] = (bok && j0 + e < key_end) ? pis[j0 + e] : -1;
+    for (int i = 0; i < 4; ++i) {
+        st.spi[i] = (bok && j0 + i < key_end && (unsigned)a[i] < (unsigned)p.max_pos) ? a[i] : -1;
+        st.spi[4 + i] = (bok && j0 + 4 + i < key_end && (unsigned)b[i] < (unsigned)p.max_pos) ? b[i] : -1;
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        if (st.spi[e] >= p.max_pos) st.spi[e] = -1;
-    const uint16_t *vb = p.v_pool + ((size_t)(bok ? blk : 0) * p.hkv + g) * D * kBlock + (j0 & 15);
+    const uint16_t *vb = bok ? p.v_pool + ((size_t)blk * p.hkv + g) * D * kBlock + (j0 & 15) : p.zero_page;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-        st.v[dt] = bok ? *reinterpret_cast<const u32x4 *>(vb + (size_t)(16 * dt + lc) * kBlock)
-                       : u32x4{0, 0, 0, 0};
+        st.v[dt] = *reinterpret_cast<const u32x4 *>(vb + (size_t)(16 * dt + lc) * kBlock);
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
-    constexpr int NC = D / 32, HALF = D / 2;
-    constexpr int WAVE_KEYS = kDecodeSplit / kWaves;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeParams p) {
+    constexpr int NC = D / 32, HALF = D / 2, NQ = HALF / 4;
+    // R(dl) for dl = 0..15, laid out [frequency quad][dl]: the 16 lanes of a
+    // lane group read one 256-byte block
+    __shared__ f32x4 s_dc[NQ][16], s_ds[NQ][16];
     __shared__ float s_o[kWaves][D][16];
     __shared__ float s_m[kWaves][16], s_l[kWaves][16];
 
@@ -141,14 +125,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     const int sp = lid % p.num_splits;
     const int r = lid / p.num_splits;
 
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lc = lane & 15, lg = lane >> 4;
+    for (int t = tid; t < NQ * 16; t += kThreads) {
+        const int dl = t & 15, q4 = t >> 4;
+        const bool in = dl < p.max_pos;
+        s_dc[q4][dl] = in ? *reinterpret_cast<const f32x4 *>(p.cos_tab + dl * HALF + 4 * q4) : f32x4{1.f, 1.f, 1.f, 1.f};
+        s_ds[q4][dl] = in ? *reinterpret_cast<const f32x4 *>(p.sin_tab + dl * HALF + 4 * q4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
     const int kv_stride = p.max_blocks * kBlock;
     const int kv_cap = min(kv_stride, p.max_kv_len);
     int kvl = p.kv_len[r];
     kvl = kvl < 0 ? 0 : (kvl > kv_cap ? kv_cap : kvl);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int lc = lane & 15, lg = lane >> 4;
-    const int wbeg = sp * kDecodeSplit + wave * WAVE_KEYS;
-    const int key_end = min(kvl, wbeg + WAVE_KEYS);
+    const int wave_keys = p.split_len / kWaves;
+    const int wbeg = sp * p.split_len + wave * wave_keys;
+    const int key_end = min(kvl, wbeg + wave_keys);
     const int32_t *bt = p.block_table + (size_t)r * p.max_blocks;
     const int32_t *pis = p.kv_pos + (size_t)r * kv_stride;
 
@@ -169,8 +161,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             u32x4 hi = *reinterpret_cast<const u32x4 *>(src + HALF + i0);
             const float *cr = p.cos_tab + (size_t)pos * HALF + i0;
             const float *sr = p.sin_tab + (size_t)pos * HALF + i0;
-            rope8(lo, hi, *reinterpret_cast<const f32x4 *>(cr), *reinterpret_cast<const f32x4 *>(cr + 4),
-                  *reinterpret_cast<const f32x4 *>(sr), *reinterpret_cast<const f32x4 *>(sr + 4));
+            rope4<0>(lo, hi, *reinterpret_cast<const f32x4 *>(cr), *reinterpret_cast<const f32x4 *>(sr));
+            rope4<1>(lo, hi, *reinterpret_cast<const f32x4 *>(cr + 4), *reinterpret_cast<const f32x4 *>(sr + 4));
             qop[c] = lo;
             qop[c + NC / 2] = hi;
         }
@@ -180,22 +172,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     f32x4 acc[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();   // R(dl) table
 
     const int nsteps = key_end > wbeg ? (key_end - wbeg + 31) / 32 : 0;
-    Step<D> cur;
-    if (nsteps > 0) step_load<D>(p, cur, bt, pis, g, wbeg, key_end, lc, lg);
-    for (int it = 0; it < nsteps; ++it) {
-        Step<D> nxt;
-        if (it + 1 < nsteps) step_load<D>(p, nxt, bt, pis, g, wbeg + 32 * (it + 1), key_end, lc, lg);
-
+    auto process = [&](Step<D> &cur) {
         f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
-            if (cur.kpi[T] >= 0) {
+            // key offset inside its block (the step start is a multiple of 32)
+            const int off = (8 * (lc >> 2) + 4 * T + (lc & 3)) & 15;
+            const int pi = cur.kpi[T];
+            const int dl = pi >= 0 ? min(off, pi) : 0;
+            const int row = pi >= 0 ? pi - dl : 0;
+            const float *cr = p.cos_tab + (size_t)row * HALF;
+            const float *sr = p.sin_tab + (size_t)row * HALF;
+            // cos/sin of 4 frequencies i0..i0+3 at pi: R(pi - dl) R(dl)
+            auto rot = [&](int i0, f32x4 &cc, f32x4 &ss) {
+                const f32x4 cp = *reinterpret_cast<const f32x4 *>(cr + i0);
+                const f32x4 sn = *reinterpret_cast<const f32x4 *>(sr + i0);
+                const f32x4 cd = s_dc[i0 >> 2][dl], sd = s_ds[i0 >> 2][dl];
+                cc = cp * cd - sn * sd;
+                ss = sn * cd + cp * sd;
+            };
 #pragma unroll
-                for (int c = 0; c < NC / 2; ++c)
-                    rope8(cur.k[T][c], cur.k[T][c + NC / 2], cur.cs[T][c][0], cur.cs[T][c][1],
-                          cur.cs[T][c][2], cur.cs[T][c][3]);
+            for (int c = 0; c < NC / 2; ++c) {
+                f32x4 c0, s0, c1, s1;
+                rot(32 * c + 8 * lg, c0, s0);
+                rot(32 * c + 8 * lg + 4, c1, s1);
+                rope4<0>(cur.k[T][c], cur.k[T][c + NC / 2], c0, s0);
+                rope4<1>(cur.k[T][c], cur.k[T][c + NC / 2], c1, s1);
             }
 #pragma unroll
             for (int c = 0; c < NC; ++c) sacc[T] = mfma16(cur.k[T][c], qop[c], sacc[T]);
@@ -229,22 +234,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         for (int e = 0; e < 4; ++e) pb[e] = pack2(sv[2 * e], sv[2 * e + 1]);
         // any unusable key in the step: zero its V channel entries so that
         // 0 * garbage cannot poison O
-        const bool wave_bad = __any(any_bad);
+        if (__any(any_bad)) {
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            u32x4 a = cur.v[dt];
-            if (wave_bad) {
+            for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    uint32_t w = a[e];
+                    uint32_t w = cur.v[dt][e];
                     if (cur.spi[2 * e] < 0) w &= 0xffff0000u;
                     if (cur.spi[2 * e + 1] < 0) w &= 0x0000ffffu;
-                    a[e] = w;
+                    cur.v[dt][e] = w;
                 }
-            }
-            acc[dt] = mfma16(a, pb, acc[dt] * alpha);
         }
-        if (it + 1 < nsteps) cur = nxt;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma16(cur.v[dt], pb, acc[dt] * alpha);
+    };
+    // two step buffers in turn; the step after the range is requested too
+    // (clamped indices, zero page) so that no branch guards the requests
+    Step<D> sa, sb;
+    if (nsteps > 0) step_load<D>(p, sa, bt, pis, g, wbeg, key_end, lc, lg);
+    for (int it = 0; it < nsteps; it += 2) {
+        step_load<D>(p, sb, bt, pis, g, wbeg + 32 * (it + 1), key_end, lc, lg);
+        process(sa);
+        if (it + 1 >= nsteps) break;
+        step_load<D>(p, sa, bt, pis, g, wbeg + 32 * (it + 2), key_end, lc, lg);
+        process(sb);
     }
 
     // ---- merge the 4 waves of the workgroup through LDS
@@ -260,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         s_l[wave][lc] = lt;
     }
     __syncthreads();
-    // thread -> (column, 8 channels)
+    // thread -> (column, D/16 channels)
     const int col = tid & 15, d0 = (tid >> 4) * (D / 16);
     if (col >= p.group) return;
     float M = -INFINITY;

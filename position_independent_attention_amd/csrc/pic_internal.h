@@ -11,7 +11,6 @@ constexpr int kBlock = 16;        // tokens per pool block
 constexpr int kTileN = 64;        // keys per staged tile in the prefill-style kernels
 constexpr int kThreads = 256;     // 4 wave64 per workgroup
 constexpr int kWaves = 4;
-constexpr int kDecodeSplit = 1024;  // keys per decode workgroup (multiple of 128)
 
 enum Mode : int { kAttn = 0, kLse = 1, kMass = 2 };
 
@@ -67,6 +66,7 @@ struct DecodeParams {
     int32_t max_pos;
     float scale_log2;
     int32_t max_kv_len;
+    int32_t split_len;        // keys per workgroup, a multiple of 4 * 32
     int32_t num_splits;
     uint16_t *out;
     float *lse;
