@@ -144,27 +144,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int32_t *bt = p.block_table + (size_t)r * p.max_blocks;
     const int32_t *pis = p.kv_pos + (size_t)r * kv_stride;
 
-    // query column lc: head g*G + lc of request r
+    // query column lc: head g*G + lc of request r (branch-free: columns past
+    // G and invalid positions rotate a clamped row and are zeroed)
     const bool qv = lc < p.group;
     const int h = g * p.group + (qv ? lc : 0);
     int pos = qv ? p.q_pos[r] : -1;
     if (pos >= p.max_pos) pos = -1;
+    const int posc = pos >= 0 ? pos : 0;
     u32x4 qop[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) qop[c] = u32x4{0, 0, 0, 0};
-    if (pos >= 0) {
+    {
         const uint16_t *src = p.q + ((size_t)r * p.hq + h) * D;
 #pragma unroll
         for (int c = 0; c < NC / 2; ++c) {
             const int i0 = 32 * c + 8 * lg;
             u32x4 lo = *reinterpret_cast<const u32x4 *>(src + i0);
             u32x4 hi = *reinterpret_cast<const u32x4 *>(src + HALF + i0);
-            const float *cr = p.cos_tab + (size_t)pos * HALF + i0;
-            const float *sr = p.sin_tab + (size_t)pos * HALF + i0;
+            const float *cr = p.cos_tab + (size_t)posc * HALF + i0;
+            const float *sr = p.sin_tab + (size_t)posc * HALF + i0;
             rope4<0>(lo, hi, *reinterpret_cast<const f32x4 *>(cr), *reinterpret_cast<const f32x4 *>(sr));
             rope4<1>(lo, hi, *reinterpret_cast<const f32x4 *>(cr + 4), *reinterpret_cast<const f32x4 *>(sr + 4));
-            qop[c] = lo;
-            qop[c + NC / 2] = hi;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qop[c] = pos >= 0 ? lo : z;
+            qop[c + NC / 2] = pos >= 0 ? hi : z;
         }
     }
 
@@ -174,7 +175,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();   // R(dl) table
 
-    const int nsteps = key_end > wbeg ? (key_end - wbeg + 31) / 32 : 0;
+    // wave-uniform step count (the compiler cannot tell on its own)
+    const int nsteps = __builtin_amdgcn_readfirstlane(key_end > wbeg ? (key_end - wbeg + 31) / 32 : 0);
     auto process = [&](Step<D> &cur) {
         f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll

@@ -769,6 +769,67 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     if (p.lse && part == 0) p.lse[row] = any ? (M + __log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
+// LSE-weighted merge for many splits and few rows (decode): one workgroup
+// per row; the split maxima / weights are staged in LDS and the splits of
+// each channel quad are spread over the workgroup's threads.
+template <int D>
+__global__ __launch_bounds__(256) void merge_many_kernel(MergeParams p) {
+    constexpr int NQ4 = D / 4;             // channel quads per row
+    constexpr int NSUB = 256 / NQ4;        // split subsets
+    __shared__ float s_w[kMergeMaxSplits];
+    __shared__ float s_red[256];
+    __shared__ f32x4 s_o[NSUB][NQ4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int S = p.num_splits;
+    float m = -INFINITY;
+    for (int s = tid; s < S; s += 256) {
+        const float v = p.part_ml[((size_t)s * p.rows + row) * 2];
+        s_w[s] = v;
+        m = fmaxf(m, v);
+    }
+    s_red[tid] = m;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (tid < off) s_red[tid] = fmaxf(s_red[tid], s_red[tid + off]);
+        __syncthreads();
+    }
+    const float M = s_red[0];
+    const float Mu = M == -INFINITY ? 0.f : M;
+    __syncthreads();
+    float l = 0.f;
+    for (int s = tid; s < S; s += 256) {
+        const float w = fast_exp2(s_w[s] - Mu);
+        s_w[s] = w;
+        l += w * p.part_ml[((size_t)s * p.rows + row) * 2 + 1];
+    }
+    s_red[tid] = l;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (tid < off) s_red[tid] += s_red[tid + off];
+        __syncthreads();
+    }
+    const float L = s_red[0];
+    const bool any = L > 0.f;
+    if (p.lse && tid == 0) p.lse[row] = any ? (M + __log2f(L)) * 0.6931471805599453f : -INFINITY;
+    if (!p.out || !p.part_o) return;
+    const int q4 = tid % NQ4, sub = tid / NQ4;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s = sub; s < S; s += NSUB)
+        o += s_w[s] * *reinterpret_cast<const f32x4 *>(p.part_o + ((size_t)s * p.rows + row) * D + 4 * q4);
+    s_o[sub][q4] = o;
+    __syncthreads();
+    if (sub != 0) return;
+#pragma unroll
+    for (int k = 1; k < NSUB; ++k) o += s_o[k][q4];
+    const float inv = any ? 1.f / L : 0.f;
+    o *= inv;
+    uint2 w;
+    w.x = pack2(o[0], o[1]);
+    w.y = pack2(o[2], o[3]);
+    *reinterpret_cast<uint2 *>(p.out + (size_t)row * D + 4 * q4) = w;
+}
+
 template <int D, int QG, int WAVES, int MODE>
 hipError_t launch_one(const FwdParams &p, hipStream_t s) {
     const int nwg = p.row_blocks * p.hkv * p.num_splits * p.batch;
@@ -805,6 +866,13 @@ hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int shape, hip
 
 hipError_t launch_merge(const MergeParams &p, int head_dim, hipStream_t s) {
     if (p.rows <= 0) return hipSuccess;
+    if (p.num_splits > 16 && p.num_splits <= kMergeMaxSplits) {
+        if (head_dim == 64)
+            hipLaunchKernelGGL(merge_many_kernel<64>, dim3(p.rows), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL(merge_many_kernel<128>, dim3(p.rows), dim3(256), 0, s, p);
+        return hipGetLastError();
+    }
     const int tpr = head_dim / 4;
     const long long threads = (long long)p.rows * tpr;
     const int grid = (int)((threads + 255) / 256);

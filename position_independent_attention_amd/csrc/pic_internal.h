@@ -8,7 +8,8 @@
 namespace pic {
 
 constexpr int kBlock = 16;        // tokens per pool block
-constexpr int kTileN = 64;        // keys per staged tile in the prefill-style kernels
+constexpr int kTileN = 64;            // keys per staged tile in the prefill-style kernels
+constexpr int kMergeMaxSplits = 4096;  // splits the many-split merge stages in LDS
 constexpr int kThreads = 256;     // 4 wave64 per workgroup
 constexpr int kWaves = 4;
 

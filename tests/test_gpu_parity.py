@@ -149,6 +149,22 @@ def test_decode_full_size_sampled():
     assert np.max(np.abs(lse.cpu().numpy()[ts, hs] - ref_l)) <= LSE_ABS
 
 
+@pytest.mark.parametrize("name", ["one_request_32k", "two_requests_9k"])
+def test_decode_many_splits(name):
+    # few (request, kv head) rows over long contexts: the key range is cut into
+    # more than 16 splits, merged by the one-workgroup-per-row merge
+    if name == "one_request_32k":
+        w = W.decode_heavy(batch=1, n_spans=32, span_tok=1024)
+    else:
+        w = W.decode_heavy(batch=2, n_spans=9, span_tok=1000, private_spans=True)
+    say(f"decode {name}: B={w.batch} kv={w.kv_len.tolist()}")
+    ctx = H.ctx_for(w)
+    out, lse, _ = H.decode(ctx, w)
+    ref_o, ref_l = oracle.attention(w)
+    compare_out(H.host_bf16(out), ref_o, "O")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+
+
 def test_decode_matches_prefill_with_one_query():
     w = W.decode_heavy(batch=4, n_spans=2, span_tok=300)
     ctx = H.ctx_for(w)
