@@ -58,9 +58,35 @@ __device__ __forceinline__ int block_excl_count(bool flag, int *s_cnt, int *tota
     return pre + below;
 }
 
+constexpr int kTopkCache = 8;   // keys per thread kept in registers: spans up to 2048 slots
+
+// Inclusive prefix sum over the 256 threads in thread order (uses s_w[4]).
+__device__ __forceinline__ int block_incl_sum(int x, int *s_w) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_w[wave] = x;
+    __syncthreads();
+    int add = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) add += w < wave ? s_w[w] : 0;
+    __syncthreads();
+    return x + add;
+}
+
+// Per-span top-k of the mass (QCFuse selection): a 4 x 8-bit radix select
+// finds the k-th largest key (masses are >= 0, so their float bits order
+// like the values), then one in-order pass keeps the keys above it and the
+// first of the keys equal to it (ties go to the lower slot index).  Spans of
+// up to 2048 slots keep their keys in registers; the digit of each pass is
+// found by a parallel suffix scan of the 256-bin histogram.
 __global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
     __shared__ int s_hist[256];
     __shared__ int s_cnt[4];
+    __shared__ int s_w[4];
     __shared__ uint32_t s_sel[2];
     const int s = blockIdx.x, tid = threadIdx.x;
     const int r = p.span_req[s], st = p.span_start[s], L = p.span_len[s];
@@ -72,43 +98,69 @@ __global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
     const int lo = max(st, 0), hi = min(st + max(L, 0), kvl);
     const int32_t *pis = p.kv_pos + (size_t)r * p.kv_stride;
     const float *mass = p.mass + (size_t)r * p.kv_stride;
+    const bool cached = hi - lo <= 256 * kTopkCache;
 
-    // candidates
-    int ncand = 0;
-    for (int base = lo; base < hi; base += 256) {
-        const int j = base + tid;
-        const bool c = j < hi && pis[j] >= 0;
-        int tot;
-        block_excl_count(c, s_cnt, &tot);
-        ncand += tot;
+    uint32_t ck[kTopkCache];
+    bool cc[kTopkCache];
+    // visit(j, key, is_candidate) over this thread's slots, in chunk order
+    auto visit = [&](auto &&f) {
+        if (cached) {
+#pragma unroll
+            for (int u = 0; u < kTopkCache; ++u) {
+                if (lo + 256 * u >= hi) break;
+                f(u, lo + 256 * u + tid, ck[u], cc[u]);
+            }
+        } else {
+            for (int u = 0, base = lo; base < hi; ++u, base += 256) {
+                const int j = base + tid;
+                const bool c = j < hi && pis[j] >= 0;
+                f(u, j, c ? __float_as_uint(mass[j]) : 0u, c);
+            }
+        }
+    };
+    int mine = 0;
+    if (cached) {
+#pragma unroll
+        for (int u = 0; u < kTopkCache; ++u) {
+            const int j = lo + 256 * u + tid;
+            const int jc = min(j, max(hi - 1, 0));   // in range for any j
+            const bool c = j < hi && pis[jc] >= 0;
+            cc[u] = c;
+            ck[u] = c ? __float_as_uint(mass[jc]) : 0u;
+            mine += c;
+        }
+    } else {
+        visit([&](int, int, uint32_t, bool c) { mine += c; });
     }
-    const int kk = min(k, ncand);
+    s_cnt[0] = 0;
+    __syncthreads();
+    if (mine) atomicAdd(&s_cnt[0], mine);
+    __syncthreads();
+    const int total = s_cnt[0];
+    __syncthreads();
+    const int kk = min(k, total);
     uint32_t thr = 0;
     int take_eq = 0;
-    bool take_all = kk == ncand;
+    const bool take_all = kk == total;
     if (!take_all) {
         uint32_t prefix = 0, pmask = 0;
         int rem = kk;
         for (int shift = 24; shift >= 0; shift -= 8) {
             s_hist[tid] = 0;
             __syncthreads();
-            for (int j = lo + tid; j < hi; j += 256) {
-                if (pis[j] < 0) continue;
-                const uint32_t key = __float_as_uint(mass[j]);
-                if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255], 1);
-            }
+            visit([&](int, int, uint32_t key, bool c) {
+                if (c && (key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255], 1);
+            });
             __syncthreads();
-            if (tid == 0) {
-                int cum = 0, dsel = 0;
-                for (int d = 255; d >= 0; --d) {
-                    if (cum + s_hist[d] >= rem) {
-                        dsel = d;
-                        break;
-                    }
-                    cum += s_hist[d];
-                }
-                s_sel[0] = (uint32_t)dsel;
-                s_sel[1] = (uint32_t)(rem - cum);
+            // thread t covers digit 255 - t: x = number of keys with that digit
+            // or a larger one; the selected digit is the one where x first
+            // reaches rem
+            const int h = s_hist[255 - tid];
+            const int x = block_incl_sum(h, s_w);
+            const int before = x - h;
+            if (before < rem && x >= rem) {
+                s_sel[0] = (uint32_t)(255 - tid);
+                s_sel[1] = (uint32_t)(rem - before);
             }
             __syncthreads();
             prefix |= s_sel[0] << shift;
@@ -122,10 +174,7 @@ __global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
     // in-order pass: larger than the threshold, or equal and among the first
     // take_eq equal ones (lowest indices)
     int out_base = 0, eq_base = 0;
-    for (int base = lo; base < hi; base += 256) {
-        const int j = base + tid;
-        bool cand = j < hi && pis[j] >= 0;
-        const uint32_t key = cand ? __float_as_uint(mass[j]) : 0u;
+    visit([&](int, int j, uint32_t key, bool cand) {
         const bool gt = cand && (take_all || key > thr);
         const bool eq = cand && !take_all && key == thr;
         int eq_tot;
@@ -136,7 +185,7 @@ __global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
         if (take && p.sel_off[s] + out_base + pos < p.max_sel) out[out_base + pos] = j;
         out_base += take_tot;
         eq_base += eq_tot;
-    }
+    });
     for (int i = kk + tid; i < k; i += 256)
         if (p.sel_off[s] + i < p.max_sel) out[i] = -1;
 }

@@ -187,6 +187,9 @@ def small_select_workloads():
                                                  q_len=32),
         "edge_spans": lambda: W.custom(110, Hq=8, Hkv=2, d=64, theta=1e4, span_lens=[[1, 2, 300, 7], [45]],
                                        q_len=[12, 5], ratio=0.34),
+        # spans longer than the 2048 slots the top-k keeps in registers
+        "long_spans": lambda: W.custom(111, Hq=8, Hkv=2, d=64, theta=1e4, span_lens=[[3000, 5], [2049, 2048]],
+                                       q_len=[8, 4], ratio=0.2),
     }
 
 
