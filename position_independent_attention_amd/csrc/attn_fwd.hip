@@ -739,6 +739,237 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     }
 }
 
+// Selection mass (QCFuse, gist.science 2604.08585, methodology B): for
+// every key j of the workgroup's range, sum over its query rows of
+// p = exp(s - lse), written per row block to mass_part.
+//
+// Unlike the attention pipeline the scores are computed untransposed,
+// S = Q K^T (the same operand registers with A and B swapped), so a lane holds
+// 4 query rows x 1 key per 16 x 16 MFMA tile.  The 8 probabilities of a lane
+// over the wave's two row tiles are then exactly its slice of a 32 (rows) x
+// 16 (keys) B operand, and the sum over the 32 rows runs on the MFMA pipe
+// against an A operand whose row 0 is ones: no cross-lane reduction.  The
+// staging (tile loads two ahead, rotation, LDS double buffer) is the
+// attention kernel's.
+template <int D, int QG, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
+    static_assert(QG == 2, "the 32-row MFMA column sum packs two row tiles");
+    using GG = Geo<D, WAVES>;
+    constexpr int BM = 16 * QG * WAVES;
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * GG::KBUF];
+    __shared__ __attribute__((aligned(16))) int32_t s_pi[2 * kTileN];
+    __shared__ float s_red[2][WAVES][kTileN];
+    __shared__ int32_t s_minpos, s_firstbad;
+    uint16_t *const Vs = nullptr;   // no V in this pass
+
+    const int nwg = p.row_blocks * p.hkv * p.num_splits * p.batch;
+    int lid = xcd_remap(blockIdx.x, nwg);
+    const int rb = lid % p.row_blocks;
+    lid /= p.row_blocks;
+    const int g = lid % p.hkv;
+    lid /= p.hkv;
+    const int sp = lid % p.num_splits;
+    const int r = lid / p.num_splits;
+
+    const int q0 = p.q_start[r];
+    const int nq = p.q_start[r + 1] - q0;
+    const int nrows = nq * p.group;
+    if (rb * BM >= nrows) return;
+    const int kv_stride = p.max_blocks * kBlock;
+    const int kv_cap = min(kv_stride, p.max_kv_len);
+    int kvl = p.kv_len[r];
+    kvl = kvl < 0 ? 0 : (kvl > kv_cap ? kv_cap : kvl);
+    const int key_begin = sp * p.split_len;
+    const int key_end = min(kvl, key_begin + p.split_len);
+    const int32_t *bt = p.block_table + (size_t)r * p.max_blocks;
+    const int32_t *pis = p.kv_pos + (size_t)r * kv_stride;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int lc = lane & 15, lg = lane >> 4;
+    if (tid == 0) {
+        s_minpos = 0x7fffffff;
+        s_firstbad = 0x7fffffff;
+    }
+    const int row0 = rb * BM + wave * 16 * QG;   // first row of this wave
+
+    // ---- A operands: query row lc of each row tile, rotated at its q_pos
+    u32x4 qop[QG][GG::NC];
+    int my_min = 0x7fffffff;
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+        const int row = row0 + 16 * qg + lc;
+        const bool valid = row < nrows;
+        const int qt = q0 + (valid ? row / p.group : 0);
+        const int qh = g * p.group + (valid ? row % p.group : 0);
+        int pos = valid ? p.q_pos[qt] : -1;
+        if (pos >= p.max_pos) pos = -1;
+        if (valid) my_min = min(my_min, pos);
+#pragma unroll
+        for (int c = 0; c < GG::NC; ++c) qop[qg][c] = u32x4{0, 0, 0, 0};
+        if (pos >= 0) {
+            const uint16_t *src = p.q + ((size_t)qt * p.hq + qh) * D;
+#pragma unroll
+            for (int c = 0; c < GG::NC / 2; ++c) {
+                const int i0 = 32 * c + 8 * lg;
+                u32x4 lo = *reinterpret_cast<const u32x4 *>(src + i0);
+                u32x4 hi = *reinterpret_cast<const u32x4 *>(src + GG::HALF + i0);
+                const float *cr = p.cos_tab + (size_t)pos * GG::HALF + i0;
+                const float *sr = p.sin_tab + (size_t)pos * GG::HALF + i0;
+                rope8(lo, hi, *reinterpret_cast<const f32x4 *>(cr), *reinterpret_cast<const f32x4 *>(cr + 4),
+                      *reinterpret_cast<const f32x4 *>(sr), *reinterpret_cast<const f32x4 *>(sr + 4));
+                qop[qg][c] = lo;
+                qop[qg][c + GG::NC / 2] = hi;
+            }
+        }
+    }
+    // ---- the rows this lane's scores belong to: 4*lg + i of each row tile
+    float lse2[QG][4];
+    int rpos[QG][4];
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = row0 + 16 * qg + 4 * lg + i;
+            const bool valid = row < nrows;
+            const int qt = q0 + (valid ? row / p.group : 0);
+            const int qh = g * p.group + (valid ? row % p.group : 0);
+            int pos = valid ? p.q_pos[qt] : -1;
+            if (pos >= p.max_pos) pos = -1;
+            rpos[qg][i] = pos;
+            float l2 = INFINITY;   // invalid rows contribute exp2(-inf) = 0
+            if (pos >= 0) {
+                const float ls = p.lse_in[(size_t)qt * p.hq + qh];
+                // -inf (nothing visible) or NaN: contribute nothing
+                l2 = (ls > -INFINITY) ? ls * 1.4426950408889634f : INFINITY;
+            }
+            lse2[qg][i] = l2;
+        }
+    const u32x4 ones_a = lc == 0 ? u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u} : u32x4{0, 0, 0, 0};
+    const float sc = p.scale_log2;
+
+    __syncthreads();
+    atomicMin(&s_minpos, my_min);
+    const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
+    Meta<D, WAVES> m1, m2;
+    Data<D, WAVES> dnext;
+    if (ntiles > 0) {
+        meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end, tid);
+        meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
+        data_load<D, WAVES>(p, dnext, m1, g, key_begin, key_end, tid, false);
+        cs_load<D, WAVES>(p, dnext, tid);
+    }
+    __syncthreads();
+    const int min_pos = s_minpos;
+    for (int j = key_begin + tid; j < key_end; j += GG::NT) {
+        const int pi = pis[j], blk = bt[j >> 4];
+        if (!(pi >= 0 && pi < p.max_pos && pi <= min_pos && blk >= 0 && blk < p.num_blocks)) {
+            atomicMin(&s_firstbad, j);
+            break;
+        }
+    }
+    __syncthreads();
+    const int first_bad = s_firstbad;
+    if (ntiles > 0) {
+        (void)data_store<D, WAVES>(dnext, Ks, Vs, s_pi, tid, false, min_pos);
+        __syncthreads();
+        data_load<D, WAVES>(p, dnext, m2, g, key_begin + kTileN, key_end, tid, false);
+        meta_load<D, WAVES>(m2, bt, pis, key_begin + 2 * kTileN, key_end, tid);
+    }
+
+    // S tile (kh, T): rows 16*qg + 4*lg + i, key column lc = LDS K row
+    // 32*kh + 16*T + lc, i.e. key 32*kh + 8*(lc/4) + 4*T + lc%4
+    auto qk = [&](const uint16_t *Kb, int kh, f32x4 (&sacc)[QG][2]) {
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) sacc[qg][0] = sacc[qg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < GG::NC; ++c) {
+            const int ch = 4 * c + lg;
+            const uint16_t *k0 = Kb + ch * (kTileN * 8) + ((lc ^ kxor<D>(ch)) * 8) + (32 * kh) * 8;
+            const u32x4 b0 = *reinterpret_cast<const u32x4 *>(k0);
+            const u32x4 b1 = *reinterpret_cast<const u32x4 *>(k0 + 16 * 8);
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) {
+                sacc[qg][0] = mfma16(qop[qg][c], b0, sacc[qg][0]);
+                sacc[qg][1] = mfma16(qop[qg][c], b1, sacc[qg][1]);
+            }
+        }
+    };
+    // probabilities of one half -> column sums of its two 16-key tiles
+    auto colsum = [&](auto full_c, const f32x4 (&sacc)[QG][2], const int32_t *pib, int kh, f32x4 (&ds)[2]) {
+        constexpr bool FULL = decltype(full_c)::value;
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            int kp = 0;
+            if constexpr (!FULL) kp = pib[32 * kh + 8 * (lc >> 2) + 4 * T + (lc & 3)];
+            u32x4 pb;
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    float pr[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int i = 2 * h2 + e;
+                        float x = fmaf(sacc[qg][T][i], sc, -lse2[qg][i]);
+                        if constexpr (!FULL) x = kp <= rpos[qg][i] ? x : -INFINITY;
+                        pr[e] = fast_exp2(x);
+                    }
+                    pb[2 * qg + h2] = pack2(pr[0], pr[1]);
+                }
+            ds[T] = mfma16(ones_a, pb, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+    };
+    auto tile_body = [&](auto more_c, auto full_c, int it) {
+        constexpr bool MORE = decltype(more_c)::value;
+        const int cur = it & 1;
+        const int tile = key_begin + it * kTileN;
+        const uint16_t *Kc = Ks + cur * GG::KBUF;
+        const int32_t *pc_ = s_pi + cur * kTileN;
+        f32x4 sA[QG][2], sB[QG][2], d0[2], d1[2];
+        qk(Kc, 0, sA);
+        qk(Kc, 1, sB);
+        colsum(full_c, sA, pc_, 0, d0);
+        if constexpr (MORE) cs_load<D, WAVES>(p, dnext, tid);
+        colsum(full_c, sB, pc_, 1, d1);
+        if (lg == 0) {
+#pragma unroll
+            for (int T = 0; T < 2; ++T) {
+                const int key = 8 * (lc >> 2) + 4 * T + (lc & 3);
+                s_red[cur][wave][key] = d0[T][0];
+                s_red[cur][wave][32 + key] = d1[T][0];
+            }
+        }
+        if constexpr (MORE)
+            (void)data_store<D, WAVES>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs, s_pi + (cur ^ 1) * kTileN, tid, false,
+                                       min_pos);
+        __syncthreads();
+        if (tid < kTileN) {
+            float tot = 0.f;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) tot += s_red[cur][w][tid];
+            const int j = tile + tid;
+            if (j < key_end) p.mass_part[(((size_t)r * p.hkv + g) * p.row_blocks + rb) * p.mass_stride + j] = tot;
+        }
+        if constexpr (MORE) {
+            data_load<D, WAVES>(p, dnext, m2, g, tile + 2 * kTileN, key_end, tid, false);
+            meta_load<D, WAVES>(m2, bt, pis, tile + 3 * kTileN, key_end, tid);
+        }
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    const int t_split = first_bad == 0x7fffffff ? ntiles : (first_bad - key_begin) / kTileN;
+    const bool last_partial = ntiles > 0 && key_end - (key_begin + (ntiles - 1) * kTileN) < kTileN;
+    const int nf = min(t_split, ntiles - 1);
+    int it = 0;
+    for (; it < nf; ++it) tile_body(T_{}, T_{}, it);
+    for (; it < ntiles - 1; ++it) tile_body(T_{}, F_{}, it);
+    if (ntiles > 0) {
+        if (t_split >= ntiles && !last_partial) tile_body(F_{}, T_{}, ntiles - 1);
+        else tile_body(F_{}, F_{}, ntiles - 1);
+    }
+}
+
 // LSE-weighted merge of split partials.  One thread per (row, 4 channels).
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
@@ -834,7 +1065,10 @@ template <int D, int QG, int WAVES, int MODE>
 hipError_t launch_one(const FwdParams &p, hipStream_t s) {
     const int nwg = p.row_blocks * p.hkv * p.num_splits * p.batch;
     if (nwg <= 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_kernel<D, QG, WAVES, MODE>), dim3(nwg), dim3(64 * WAVES), 0, s, p);
+    if constexpr (MODE == kMass && QG == 2)
+        hipLaunchKernelGGL((mass_kernel<D, QG, WAVES>), dim3(nwg), dim3(64 * WAVES), 0, s, p);
+    else
+        hipLaunchKernelGGL((fwd_kernel<D, QG, WAVES, MODE>), dim3(nwg), dim3(64 * WAVES), 0, s, p);
     return hipGetLastError();
 }
 
