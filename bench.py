@@ -24,8 +24,18 @@ precision CPU oracle, single-threaded, timed on a sample of step 1's rows and
 scaled by visible (row, key) pairs to the whole step.
 
     python bench.py [--steps K] [--warmup W]
+
+HBM traffic of the dominant kernel (roofline.traffic) comes from two
+rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) of this script, each scaled by
+what the same counter reads for a plain device copy of known size
+(--calibrate-copy); --traffic-from turns the four runs into
+profiles/prefill_traffic.json, which records a hash of the kernel sources:
+the field is null once those sources differ from the measured ones.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -37,6 +47,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attended KV tokens/s + % of HBM/MFMA roofline (GQA 32q/8kv, d=128)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+TRAFFIC_KERNEL = "fwd_kernel<128, 2, 8, 0>"
+# the files whose change invalidates a traffic measurement of that kernel
+TRAFFIC_SOURCES = ["position_independent_attention_amd/csrc/attn_fwd.hip",
+                   "position_independent_attention_amd/csrc/pic_internal.h",
+                   "position_independent_attention_amd/csrc/api.cpp",
+                   "position_independent_attention_amd/build.py"]
+COPY_BYTES = 512 << 20
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
@@ -56,6 +74,76 @@ def visible_pairs(w):
     return tot
 
 
+def sources_hash():
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Bytes per launch from profiles/prefill_traffic.json, or None if absent or
+    taken from other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256") != sources_hash():
+        return None
+    return int(t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"])
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of COPY_BYTES, 10 times (for the counter
+    calibration run)."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.randint(0, 255, (COPY_BYTES,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes": COPY_BYTES, "launches": 10}), flush=True)
+
+
+def _pmc(d, counter, name_part, every=1):
+    """Mean counter value over the dispatches of kernels named like name_part
+    (every: take every n-th of them in dispatch order, from the first)."""
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                rows.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    rows = sorted(rows)[::every]
+    if not rows:
+        raise SystemExit(f"no {counter} rows for '{name_part}' under {d}")
+    return float(np.mean([v for _, v in rows])), len(rows)
+
+
+def traffic_from(copy_fetch, copy_write, fetch, write):
+    """Scale the kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by the
+    reading of the same counters for the calibration copy."""
+    cf, _ = _pmc(copy_fetch, "FETCH_SIZE", "copyBuffer")
+    cw, _ = _pmc(copy_write, "WRITE_SIZE", "copyBuffer")
+    # each step launches the kernel twice (step 1, then the pass over the fused
+    # cache): the step-1 dispatches are every other one from the first
+    kf, nf = _pmc(fetch, "FETCH_SIZE", TRAFFIC_KERNEL, every=2)
+    kw, nw = _pmc(write, "WRITE_SIZE", TRAFFIC_KERNEL, every=2)
+    ff, fw = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
+    out = {"kernel": TRAFFIC_KERNEL, "workload": "long_context_qc_fusion step 1 (pic_attn_prefill)",
+           "sources_sha256": sources_hash(),
+           "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": COPY_BYTES,
+           "fetch_scale": ff, "write_scale": fw,
+           "kernel_fetch_kib": kf, "kernel_write_kib": kw, "dispatches": [nf, nw],
+           "fetch_bytes_per_launch": kf * 1024.0 * ff, "write_bytes_per_launch": kw * 1024.0 * fw}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out), flush=True)
+
+
 def attended_tokens(w):
     return int(sum(int((w.kv_pos[r, :w.kv_len[r]] >= 0).sum()) for r in range(w.batch)))
 
@@ -70,7 +158,14 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-private", action="store_true",
                     help="decode line on the unshared control (4 GiB pool)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the device copy the traffic counters are scaled by")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
+                    help="rocprofv3 --pmc output dirs -> profiles/prefill_traffic.json")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see the design notes "
               "for how it would shard); run with --gpus 1", file=sys.stderr)
@@ -80,6 +175,9 @@ def main():
     from position_independent_attention_amd import pic, workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -159,9 +257,10 @@ def main():
     pairs = visible_pairs(w)
     flops = pairs * w.num_q_heads * 4 * w.head_dim
     achieved = flops / (op_ms["prefill"] / 1e3) / 1e12
-    roofline = {"kernel": "pic_attn_prefill (fwd_kernel<128,4,attn> + split merge), step 1",
+    roofline = {"kernel": "pic_attn_prefill, step 1: fwd_kernel<128, 2, 8, 0> (split partials) + merge_kernel; "
+                          "the duration is the whole call's",
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                 "algorithmic_flops": flops, "avg_ms": round(op_ms["prefill"], 5)}
 
     result = {"metric": METRIC, "value": round(value, 1), "unit": "attended KV tokens/s", "n_gpus": 1,
