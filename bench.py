@@ -167,8 +167,9 @@ def main():
         traffic_from(*args.traffic_from)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see the design notes "
-              "for how it would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (requests and kv heads "
+              "shard without exchange; a split KV range needs one exchange of partial O + LSE); "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
