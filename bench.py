@@ -156,6 +156,7 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-recompute", action="store_true")
     ap.add_argument("--decode-private", action="store_true",
                     help="decode line on the unshared control (4 GiB pool)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -274,6 +275,44 @@ def main():
                          "rope_theta": w.rope_theta, "select_ratio": w.ratio, "fused_rows": nsel,
                          "step": "prefill+lse, qc_score_select, kv_fuse_scatter, prefill(fused), decode(1)"},
               "roofline": roofline, "ops_ms": {k: round(v, 5) for k, v in op_ms.items()}}
+
+    if not args.no_recompute:
+        # Discrete-token recompute (QCFuse's sparse recompute): the 4,928 selected
+        # tokens as queries at their own logical positions over the fused cache.
+        step()   # leaves the fused cache and this step's selection in `sel`
+        torch.cuda.synchronize()
+        pos_r = np.sort(kv_pos0.cpu().numpy()[0, sel.cpu().numpy()]).astype(np.int32)
+        qr = t(W.fresh_queries(nsel, w.num_q_heads, w.head_dim, seed=7))
+        dcr = pic.DeviceCache(dc.pool_k, dc.pool_v, dc.block_table, dc.kv_len, dc.kv_pos, kv_fused,
+                              q=qr, q_start=t(np.array([0, nsel], np.int32)), q_pos=t(pos_r),
+                              total_q=nsel, max_q_len=nsel)
+        outr = torch.empty((nsel, w.num_q_heads, w.head_dim), dtype=torch.int16, device=dev)
+        wsr = torch.empty(max(1, pic.pic_workspace_bytes(ctx, pic.PIC_OP_PREFILL, dcr.req(), nsel, nsel)),
+                          dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            pic.pic_attn_prefill(ctx, dcr, outr, None, ws=wsr, stream=stream)
+        torch.cuda.synchronize()
+        reps = 10
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            pic.pic_attn_prefill(ctx, dcr, outr, None, ws=wsr, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rms = e0.elapsed_time(e1) / reps
+        fpi = dc.kv_pos.cpu().numpy()[0, :kv_fused]
+        fpi = np.sort(fpi[fpi >= 0])
+        pairs_r = int(np.searchsorted(fpi, pos_r, side="right").sum())
+        flops_r = pairs_r * w.num_q_heads * 4 * w.head_dim
+        result["sparse_recompute"] = {
+            "workload": f"{nsel} selected tokens as queries at their logical positions over the fused "
+                        f"{kv_fused}-slot cache, causal by position",
+            "ms_per_call": round(rms, 5), "visible_pairs": pairs_r,
+            "roofline": {"bound": "mfma", "achieved": round(flops_r / (rms / 1e3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops_r / (rms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "algorithmic_flops": flops_r}}
+        del dcr, outr, wsr
 
     if not args.no_decode:
         wd = W.decode_heavy(private_spans=args.decode_private)

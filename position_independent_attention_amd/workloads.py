@@ -378,6 +378,34 @@ def custom(seed: int, *, Hq: int, Hkv: int, d: int, theta: float, span_lens: Seq
                     decode=decode, max_position=max_position, rng=rng)
 
 
+
+def fresh_queries(n: int, Hq: int, d: int, seed: int) -> np.ndarray:
+    """n recomputed query tokens, N(0,1) rounded to bf16 bits [n][Hq][d]."""
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(rng.standard_normal((n, Hq, d), dtype=np.float32))
+
+
+def recompute_queries(w: Workload, q_pos_per_req: Sequence[np.ndarray], seed: int) -> Workload:
+    """Discrete-token recompute (QCFuse's sparse recompute): each request's
+    recomputed tokens become its query tokens at their own logical positions,
+    over the cache held in `w` (normally the fused cache).  Fresh queries are
+    N(0,1) rounded to bf16; a request's queries are ordered by position (any
+    order gives the same per-query result).  The returned workload shares w's
+    cache arrays and spans."""
+    pos = [np.sort(np.asarray(p, np.int32)) for p in q_pos_per_req]
+    assert len(pos) == w.batch
+    q_start = np.zeros(w.batch + 1, np.int32)
+    q_start[1:] = np.cumsum([len(p) for p in pos])
+    n = int(q_start[-1])
+    q = fresh_queries(n, w.num_q_heads, w.head_dim, seed)
+    out = dataclasses.replace(w)
+    out.name = w.name + "_recompute"
+    out.q = q
+    out.q_start = q_start
+    out.q_pos = np.concatenate(pos).astype(np.int32) if n else np.zeros(0, np.int32)
+    out.decode = False
+    return out
+
 CONFIGS = {
     "tiny": tiny,
     "llama_layer": llama_layer,

@@ -319,6 +319,51 @@ def test_fuse_full_size_with_seeded_selection():
     assert np.max(np.abs(lse2.cpu().numpy()[ts, hs] - refl2)) <= LSE_ABS
 
 
+# ------------------------------------------------------- sparse recompute
+
+def _recompute_case(w, sel_idx, req_off, seed):
+    """The oracle's fused cache, queried by the selected tokens at their
+    pre-fusion logical positions (QCFuse's discrete-token recompute)."""
+    n = int(req_off[-1])
+    pk, pv, kp, kl = oracle.fuse(w, sel_idx, req_off, w.fresh_k[:n], w.fresh_v[:n])
+    fused = w.copy()
+    fused.pool_k, fused.pool_v, fused.kv_pos, fused.kv_len = pk, pv, kp, kl
+    pos = [w.kv_pos[r, sel_idx[req_off[r]:req_off[r + 1]]] for r in range(w.batch)]
+    return W.recompute_queries(fused, pos, seed)
+
+
+@pytest.mark.parametrize("name", ["tiny", "long_context_small", "shared_small", "edge_spans"])
+def test_recompute_parity(name):
+    """Scattered query positions, causal by position, over the fused cache:
+    every recomputed token sees the context before it and its own fresh row."""
+    w = small_select_workloads()[name]()
+    ref_off, ref_idx = oracle.select(w, oracle.mass(w))
+    wr = _recompute_case(w, ref_idx, H.req_offsets(w, ref_off), 900)
+    say(f"recompute {name}: queries per request {np.diff(wr.q_start).tolist()}")
+    ctx = H.ctx_for(wr)
+    out, lse, _ = H.prefill(ctx, wr)
+    ref_o, ref_l = oracle.attention(wr)
+    compare_out(H.host_bf16(out), ref_o, "O recompute")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+
+
+def test_recompute_full_size_sampled():
+    """Long-context shape: 4,928 selected tokens (seeded, 154 per span) as
+    queries over the fused 37,952-slot cache; sampled rows against the oracle."""
+    w = W.long_context()
+    rng = np.random.default_rng(45)
+    sel = np.concatenate([np.sort(rng.choice(np.arange(st, st + L), size=154, replace=False))
+                          for st, L in zip(w.span_start, w.span_len)]).astype(np.int32)
+    wr = _recompute_case(w, sel, np.array([0, len(sel)], np.int32), 901)
+    ctx = H.ctx_for(wr)
+    out, lse, _ = H.prefill(ctx, wr)
+    ts = np.array([0, 1, 999, 2500, 4927, 3333, 17, 4000])
+    hs = np.array([0, 31, 5, 17, 9, 22, 3, 12])
+    ref_o, ref_l = oracle.attention(wr, (ts, hs))
+    compare_out(H.host_bf16(out)[ts, hs], ref_o, "O recompute sampled")
+    assert np.max(np.abs(lse.cpu().numpy()[ts, hs] - ref_l)) <= LSE_ABS
+
+
 # ------------------------------------------------------- sharing / repeat
 
 def test_shared_pool_untouched_and_runs_bitwise_repeatable():

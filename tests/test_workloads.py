@@ -87,3 +87,17 @@ def test_decode_offsets_not_block_aligned():
     w = SMALL["decode_heavy"]()
     assert np.any(w.kv_pos[:, 0] % 16 != 0)
     assert np.all(np.diff(w.q_start) == 1)
+
+
+def test_recompute_queries_layout():
+    w = W.tiny()
+    pos = [np.array([456, 3, 200, 17], np.int32)]
+    a = W.recompute_queries(w, pos, seed=5)
+    b = W.recompute_queries(w, pos, seed=5)
+    assert a.q.shape == (4, w.num_q_heads, w.head_dim) and a.q.dtype == np.uint16
+    assert np.array_equal(a.q, b.q)                       # seeded
+    assert a.q_pos.tolist() == [3, 17, 200, 456]          # ordered by position
+    assert a.q_start.tolist() == [0, 4]
+    assert a.pool_k is w.pool_k and a.kv_pos is w.kv_pos  # cache shared, not copied
+    e = W.recompute_queries(w, [np.zeros(0, np.int32)], seed=5)
+    assert e.total_q == 0 and e.q_start.tolist() == [0, 0]
