@@ -60,6 +60,8 @@ def lib() -> C.CDLL:
         h.oracle_attention.restype = C.c_int
         h.oracle_mass.argtypes = [C.POINTER(_Problem), C.c_int32, _f64p]
         h.oracle_mass.restype = C.c_int
+        h.oracle_key_norm.argtypes = [C.POINTER(_Problem), C.c_int32, _f64p]
+        h.oracle_key_norm.restype = C.c_int
         h.oracle_select.argtypes = [C.c_int32, _i32p, _i32p, _i32p, C.c_double, _f64p, C.c_int32,
                                     _i32p, _i32p, _i32p, _i32p, C.c_int32]
         h.oracle_select.restype = C.c_int32
@@ -132,8 +134,21 @@ def mass(w) -> np.ndarray:
     return m
 
 
+def key_norm(w) -> np.ndarray:
+    """Anchor score [B, max_blocks*16] in float64: squared norm of each usable
+    slot's stored key over all kv heads (zero beyond kv_len and for unusable
+    slots)."""
+    keep: list = []
+    p = _problem(w, keep)
+    stride = int(np.asarray(w.kv_pos).shape[1])
+    m = np.zeros((int(np.asarray(w.kv_len).shape[0]), stride), np.float64)
+    lib().oracle_key_norm(C.byref(p), stride, _ptr(m, _f64p))
+    return m
+
+
 def select(w, mass_arr: np.ndarray, ratio: Optional[float] = None):
-    """Per-span top fraction: (sel_off [n_spans+1], sel_idx [total])."""
+    """Per-span top fraction of the score mass_arr (selection mass or anchor
+    key norm): (sel_off [n_spans+1], sel_idx [total])."""
     ratio = float(w.ratio if ratio is None else ratio)
     sr = np.ascontiguousarray(w.span_req, np.int32)
     ss = np.ascontiguousarray(w.span_start, np.int32)

@@ -30,6 +30,8 @@
  *  - Selection: per span, the k = min(#candidates, floor(ratio*L + 0.5))
  *    tokens of largest mass, ties to the lower sequence index, listed in
  *    ascending index order.
+ *  - Anchors: per span, the tokens with the largest squared key norm (all kv
+ *    heads), selected like the mass (see oracle_key_norm).
  *  - Fusion: recomputed rows are mixed back into the cache [QCFuse (es),
  *    "Lo esencial" step 4; QCFuse (de), methodik phase 4] without ever
  *    writing a shared block [MiniPIC section 2.1, benefit paragraph]: fresh
@@ -303,6 +305,40 @@ int oracle_mass(const oracle_problem *p, int32_t stride, double *mass)
     free(visible);
     free(s);
     free(prob);
+    return 0;
+}
+
+/*
+ * Anchor score: the squared norm of each cached token's stored (unrotated)
+ * key, summed over every kv head and every dimension; 0 for slots that hold no
+ * usable key (pi < 0 or no block).  The pages pick anchor tokens as the small
+ * fraction with the highest key norms [QCFuse (es), methodology A, anchor
+ * extraction; QCFuse (de), methodik phase 1]; which heads and whether rotated
+ * are not stated.  Reading: the whole key vector of the token (all kv heads);
+ * RoPE is a rotation, so rotated or not gives the same norm.  Ranking by the
+ * squared norm is ranking by the norm.  Written for j < kv_len[r] into
+ * norm[r * stride + j]; other entries untouched.
+ */
+int oracle_key_norm(const oracle_problem *p, int32_t stride, double *norm)
+{
+    int32_t d = p->head_dim;
+    double *x = (double *)malloc(sizeof(double) * d);
+    for (int32_t r = 0; r < p->batch; ++r) {
+        for (int32_t j = 0; j < p->kv_len[r]; ++j) {
+            int32_t pi = p->kv_pos[(int64_t)r * kv_stride(p) + j];
+            int32_t blk = slot_block(p, r, j);
+            double acc = 0.0;
+            if (pi >= 0 && blk >= 0) {
+                for (int32_t g = 0; g < p->num_kv_heads; ++g) {
+                    load_key(p, blk, g, j % ORACLE_BLOCK, x);
+                    for (int32_t i = 0; i < d; ++i)
+                        acc += x[i] * x[i];
+                }
+            }
+            norm[(int64_t)r * stride + j] = acc;
+        }
+    }
+    free(x);
     return 0;
 }
 

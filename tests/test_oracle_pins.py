@@ -423,6 +423,62 @@ def test_planted_needles_are_selected():
         assert m2[0, j] < 0.5 * m[0, j]
 
 
+# ------------------------------------------------------ anchor key norm
+
+def _slot(w, r, j):
+    return int(w.block_table[r, j // BLOCK]), j % BLOCK
+
+
+def test_key_norm_closed_form_per_head():
+    """A slot whose key is the constant c_g on kv head g has squared norm
+    d * sum_g c_g^2: every head counts, once (a dropped head, a mean over heads
+    or a per-head maximum would all differ)."""
+    w = W.custom(121, Hq=8, Hkv=4, d=64, theta=1e4, span_lens=[[40]], q_len=[2])
+    consts = [0.5, -1.25, 2.0, 0.0]   # bf16-exact
+    blk, off = _slot(w, 0, 7)
+    for g, c in enumerate(consts):
+        w.pool_k[blk, g, off, :] = W.f32_to_bf16_bits(np.full(64, c, np.float32))
+    n = oracle.key_norm(w)
+    assert n[0, 7] == 64 * sum(c * c for c in consts)
+
+
+def test_key_norm_rotation_invariant_and_scaling():
+    """RoPE is a rotation: the norm of the key rotated at its pi (through the
+    oracle's own rope) equals the stored key's norm; doubling a key (exact in
+    bf16) multiplies the squared norm by exactly 4."""
+    w = W.tiny()
+    n = oracle.key_norm(w)
+    for j in (0, 3, 130, 255):
+        blk, off = _slot(w, 0, j)
+        tot = 0.0
+        for g in range(w.num_kv_heads):
+            k = f32(w.pool_k[blk, g, off]).astype(np.float64)
+            tot += float(np.sum(oracle.rope(w.head_dim, w.rope_theta, int(w.kv_pos[0, j]), k) ** 2))
+        assert abs(tot - n[0, j]) <= 1e-9 * n[0, j]
+    w2 = w.copy()
+    blk, off = _slot(w2, 0, 9)
+    w2.pool_k[blk, :, off] = W.f32_to_bf16_bits(2.0 * f32(w2.pool_k[blk, :, off]))
+    assert oracle.key_norm(w2)[0, 9] == 4.0 * n[0, 9]
+
+
+def test_key_norm_masked_slots_and_planted_anchors():
+    """Unusable slots score 0 and are never anchors; keys planted with a 4x
+    larger scale are the anchors of their spans."""
+    w = W.tiny()
+    w.kv_pos[0, 20:24] = -1
+    planted = {0: [3, 50, 99], 128: [130, 201, 250]}   # span start -> slots
+    for js in planted.values():
+        for j in js:
+            blk, off = _slot(w, 0, j)
+            w.pool_k[blk, :, off] = W.f32_to_bf16_bits(4.0 * f32(w.pool_k[blk, :, off]))
+    n = oracle.key_norm(w)
+    assert np.all(n[0, 20:24] == 0.0)
+    off_, idx = oracle.select(w, n, ratio=3 / 128)   # k = 3 per span
+    assert idx.tolist() == sorted(sum(planted.values(), []))
+    big = oracle.select(w, n, ratio=1.0)[1]
+    assert not set(range(20, 24)) & set(big.tolist())
+
+
 # ---------------------------------------------------------------- fusion
 
 def test_fuse_semantics_against_replaced_dense_rows():
