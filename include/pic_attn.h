@@ -60,7 +60,8 @@ typedef enum {
 typedef enum {
     PIC_OP_PREFILL = 0,
     PIC_OP_DECODE = 1,
-    PIC_OP_SELECT = 2
+    PIC_OP_SELECT = 2,
+    PIC_OP_ANCHOR = 3
 } pic_op;
 
 /* Model geometry and RoPE parameters.  RoPE pairs element i with i + d/2 and
@@ -147,7 +148,9 @@ const char *pic_ctx_last_error(const pic_ctx *ctx);
 
 /* Bytes of device workspace that `op` needs for these sizes (0 is possible).
  * For PIC_OP_DECODE total_q and max_q_len are ignored (one query per request).
- * For PIC_OP_SELECT the figure covers the case lse == NULL and mass == NULL. */
+ * For PIC_OP_SELECT the figure covers the case lse == NULL and mass == NULL.
+ * For PIC_OP_ANCHOR total_q and max_q_len are ignored; the figure covers
+ * norm == NULL. */
 pic_status pic_workspace_bytes(const pic_ctx *ctx, pic_op op, const pic_req_table *req,
                                int32_t total_q, int32_t max_q_len, size_t *bytes);
 
@@ -193,6 +196,25 @@ pic_status qc_score_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
                            const pic_queries *qs, const float *lse, const pic_spans *spans,
                            int32_t max_sel, int32_t *sel_idx, float *mass, void *ws,
                            size_t ws_bytes, void *stream);
+
+/* Anchor extraction ([QCFuse] methodology A, "Extraccion de Anclajes"; phase 1
+ * of the German page): the tokens of a context chunk with the highest key
+ * norms.  score_r[j] = sum over kv heads g and dims i of k~_j[g][i]^2, the
+ * squared norm of slot j's stored (unrotated) key -- RoPE preserves norms --,
+ * 0 for slots that hold no usable key (pi outside [0, max_position), or a
+ * block id outside the pool); then per span the k_s slots of largest score (ties to the lower slot
+ * index), among slots with pi >= 0, written to sel_idx[sel_off[s] ..] in
+ * ascending order, -1 past the candidates (the same rule as qc_score_select).
+ * Reads only K; needs no queries.
+ *   sel_idx: device int32 [sel_off[n_spans]]
+ *   norm:    device fp32 [batch][max_blocks * 16] or NULL; entries
+ *            j < kv_len[r] are written.
+ *   max_sel: host-side value of sel_off[n_spans] (bounds sel_idx).
+ *   ws:      device workspace of at least pic_workspace_bytes(PIC_OP_ANCHOR)
+ *            (0 bytes when norm is given). */
+pic_status qc_anchor_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_table *req,
+                            const pic_spans *spans, int32_t max_sel, int32_t *sel_idx, float *norm,
+                            void *ws, size_t ws_bytes, void *stream);
 
 /* Cache fusion ([QCFuse] "Lo esencial" step 4 and phase 4: recomputed tokens
  * mixed into the stored cache) without writing shared blocks ([MiniPIC]

@@ -271,6 +271,11 @@ void pic_ctx_destroy(pic_ctx *ctx) {
     delete ctx;
 }
 
+// Anchor extraction: the per-slot score when the caller passes no buffer.
+size_t anchor_ws(int batch, int max_blocks) {
+    return align_up((size_t)batch * max_blocks * kBlock * sizeof(float));
+}
+
 pic_status pic_workspace_bytes(const pic_ctx *ctx, pic_op op, const pic_req_table *req, int32_t total_q,
                                int32_t max_q_len, size_t *bytes) {
     if (!ctx || !req || !bytes) return PIC_ERR_INVALID_ARG;
@@ -291,6 +296,9 @@ pic_status pic_workspace_bytes(const pic_ctx *ctx, pic_op op, const pic_req_tabl
         *bytes = select_ws(c, pl, req->batch, req->max_blocks, total_q, req->max_kv_len).total;
         return PIC_OK;
     }
+    case PIC_OP_ANCHOR:
+        *bytes = anchor_ws(req->batch, req->max_blocks);
+        return PIC_OK;
     }
     return PIC_ERR_INVALID_ARG;
 }
@@ -473,6 +481,58 @@ pic_status qc_score_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
     if (max_sel > 0) {
         e = pic::launch_topk(sp, s);
         if (e != hipSuccess) return hip_fail(ctx, e, "top-k launch");
+    }
+    return PIC_OK;
+}
+
+pic_status qc_anchor_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_table *req,
+                            const pic_spans *spans, int32_t max_sel, int32_t *sel_idx, float *norm, void *ws,
+                            size_t ws_bytes, void *stream) {
+    if (check_ctx(ctx) != PIC_OK) return PIC_ERR_INVALID_ARG;
+    pic_status st = check_pool_req(ctx, pool, req);
+    if (st != PIC_OK) return st;
+    if (!spans || spans->n_spans < 0) return fail(ctx, PIC_ERR_INVALID_ARG, "spans descriptor invalid%s");
+    if (spans->n_spans > 0 && (!spans->span_req || !spans->span_start || !spans->span_len || !spans->sel_off))
+        return fail(ctx, PIC_ERR_INVALID_ARG, "span arrays are NULL%s");
+    if (max_sel < 0 || (max_sel > 0 && !sel_idx)) return fail(ctx, PIC_ERR_INVALID_ARG, "sel_idx / max_sel invalid%s");
+    if (req->batch > 65535) return fail(ctx, PIC_ERR_UNSUPPORTED, "anchor extraction supports up to 65535 requests%s");
+    if (req->batch == 0) return PIC_OK;
+    const size_t need = norm ? 0 : anchor_ws(req->batch, req->max_blocks);
+    if (need > 0 && (!ws || ws_bytes < need)) return fail(ctx, PIC_ERR_WORKSPACE, "workspace too small for anchors%s");
+    const pic_config &c = ctx->cfg;
+    hipStream_t s = (hipStream_t)stream;
+    float *score = norm ? norm : (float *)ws;
+    pic::NormParams np;
+    std::memset(&np, 0, sizeof np);
+    np.k_pool = pool->k;
+    np.num_blocks = pool->num_blocks;
+    np.hkv = c.num_kv_heads;
+    np.block_table = req->block_table;
+    np.kv_len = req->kv_len;
+    np.kv_pos = req->kv_pos;
+    np.max_blocks = req->max_blocks;
+    np.max_pos = c.max_position;
+    np.batch = req->batch;
+    np.norm = score;
+    hipError_t e = pic::launch_key_norm(np, c.head_dim, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "key norm launch");
+    if (max_sel > 0) {
+        pic::SelectParams sp;
+        std::memset(&sp, 0, sizeof sp);
+        sp.kv_len = req->kv_len;
+        sp.kv_pos = req->kv_pos;
+        sp.kv_stride = req->max_blocks * kBlock;
+        sp.batch = req->batch;
+        sp.mass = score;
+        sp.span_req = spans->span_req;
+        sp.span_start = spans->span_start;
+        sp.span_len = spans->span_len;
+        sp.sel_off = spans->sel_off;
+        sp.n_spans = spans->n_spans;
+        sp.sel_idx = sel_idx;
+        sp.max_sel = max_sel;
+        e = pic::launch_topk(sp, s);
+        if (e != hipSuccess) return hip_fail(ctx, e, "anchor top-k launch");
     }
     return PIC_OK;
 }

@@ -100,6 +100,18 @@ struct SelectParams {
     int32_t max_sel;          // capacity of sel_idx (host value)
 };
 
+// Anchor key norms (QCFuse anchor extraction).
+struct NormParams {
+    const uint16_t *k_pool;
+    int32_t num_blocks, hkv;
+    const int32_t *block_table;
+    const int32_t *kv_len;
+    const int32_t *kv_pos;
+    int32_t max_blocks, max_pos;
+    int32_t batch;
+    float *norm;              // [B][max_blocks * 16]
+};
+
 struct FuseParams {
     uint16_t *k_pool;
     uint16_t *v_pool;
@@ -125,6 +137,7 @@ hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t s);
 hipError_t launch_merge(const MergeParams &p, int head_dim, hipStream_t s);
 hipError_t launch_mass_reduce(const SelectParams &p, hipStream_t s);
 hipError_t launch_topk(const SelectParams &p, hipStream_t s);
+hipError_t launch_key_norm(const NormParams &p, int head_dim, hipStream_t s);
 hipError_t launch_fuse(const FuseParams &p, int head_dim, hipStream_t s);
 
 }  // namespace pic

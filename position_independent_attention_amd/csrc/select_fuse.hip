@@ -257,7 +257,62 @@ __global__ void fuse_len_kernel(FuseParams p) {
     p.kv_len[r] = min(base + cnt, kv_stride);
 }
 
+// Anchor score of every slot of a request (QCFuse, gist.science 2604.08585,
+// methodology A / phase 1: anchors are the tokens with the highest key norms):
+// the squared norm of the stored (unrotated) key over all kv heads, 0 for
+// unusable slots.  One workgroup per 16-slot block, each wave 4 slots; a lane
+// sums the squares of its 16-byte chunks of the slot's key (bf16 squares are
+// exact in fp32) and a fixed-order butterfly adds the lanes: deterministic.
+// HBM-bound: every usable key is read once.
+template <int D>
+__global__ __launch_bounds__(256) void key_norm_kernel(NormParams p) {
+    const int b = blockIdx.x, r = blockIdx.y;
+    const int kv_stride = p.max_blocks * kBlock;
+    int kvl = p.kv_len[r];
+    kvl = kvl < 0 ? 0 : (kvl > kv_stride ? kv_stride : kvl);
+    if (b * kBlock >= kvl) return;
+    const int blk = p.block_table[(size_t)r * p.max_blocks + b];
+    const bool bok = (unsigned)blk < (unsigned)p.num_blocks;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr int CPR = D / 8;               // 16-byte chunks per head row
+    const int nch = p.hkv * CPR;             // chunks of one slot's key
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int off = 4 * wave + u, j = b * kBlock + off;
+        if (j >= kvl) break;                 // wave-uniform
+        const int pi = p.kv_pos[(size_t)r * kv_stride + j];
+        const bool ok = bok && (unsigned)pi < (unsigned)p.max_pos;
+        float acc = 0.f;
+        if (ok) {
+            for (int c = lane; c < nch; c += 64) {
+                const int g = c / CPR, cc = c % CPR;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                    p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + off) * D + 8 * cc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = __uint_as_float(v[e] << 16), hi = __uint_as_float(v[e] & 0xffff0000u);
+                    acc = fmaf(lo, lo, acc);
+                    acc = fmaf(hi, hi, acc);
+                }
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+        if (lane == 0) p.norm[(size_t)r * kv_stride + j] = ok ? acc : 0.f;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_key_norm(const NormParams &p, int head_dim, hipStream_t s) {
+    if (p.batch <= 0 || p.max_blocks <= 0) return hipSuccess;
+    const dim3 grid(p.max_blocks, p.batch);
+    if (head_dim == 64)
+        hipLaunchKernelGGL(key_norm_kernel<64>, grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL(key_norm_kernel<128>, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_mass_reduce(const SelectParams &p, hipStream_t s) {
     if (p.batch <= 0 || p.mass_stride <= 0) return hipSuccess;

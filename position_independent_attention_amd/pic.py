@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpicattn.so")
 
 PIC_OK, PIC_ERR_INVALID_ARG, PIC_ERR_UNSUPPORTED, PIC_ERR_WORKSPACE, PIC_ERR_HIP = range(5)
-PIC_OP_PREFILL, PIC_OP_DECODE, PIC_OP_SELECT = range(3)
+PIC_OP_PREFILL, PIC_OP_DECODE, PIC_OP_SELECT, PIC_OP_ANCHOR = range(4)
 PIC_BLOCK_SIZE = 16
 
 _vp = C.c_void_p
@@ -90,6 +90,9 @@ def lib() -> C.CDLL:
         h.qc_score_select.argtypes = [_vp, P(PicKvPool), P(PicReqTable), P(PicQueries), _vp, P(PicSpans),
                                       _i32, _vp, _vp, _vp, C.c_size_t, _vp]
         h.qc_score_select.restype = C.c_int
+        h.qc_anchor_select.argtypes = [_vp, P(PicKvPool), P(PicReqTable), P(PicSpans), _i32, _vp, _vp, _vp,
+                                       C.c_size_t, _vp]
+        h.qc_anchor_select.restype = C.c_int
         h.kv_fuse_scatter.argtypes = [_vp, P(PicKvPool), P(PicReqTable), _vp, _vp, _vp, _vp, _i32, _i32, _vp]
         h.kv_fuse_scatter.restype = C.c_int
         _lib = h
@@ -253,6 +256,17 @@ def qc_score_select(ctx: Context, dc: DeviceCache, lse, max_sel: int, sel_idx, m
                                int(max_sel), _ptr(sel_idx), _ptr(mass), _ptr(ws), ws.numel(), _stream(stream))
     _check(ctx, st, "qc_score_select")
     return sel_idx, mass
+
+
+def qc_anchor_select(ctx: Context, dc: DeviceCache, max_sel: int, sel_idx, norm=None, ws=None, stream=None):
+    """Per-span anchors by stored-key norm (dc.sel_off holds the per-span budget
+    CSR, e.g. from pic_select_offsets with the anchor fraction)."""
+    pool, req, sp = dc.pool(), dc.req(), dc.spans()
+    ws, _ = _workspace(ctx, PIC_OP_ANCHOR, req, 0, 0, ws, dc.pool_k.device)
+    st = lib().qc_anchor_select(ctx.handle, C.byref(pool), C.byref(req), C.byref(sp), int(max_sel), _ptr(sel_idx),
+                                _ptr(norm), _ptr(ws), ws.numel(), _stream(stream))
+    _check(ctx, st, "qc_anchor_select")
+    return sel_idx, norm
 
 
 def kv_fuse_scatter(ctx: Context, dc: DeviceCache, sel_idx, sel_req_off, k_new, v_new, n_sel: int,

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     h = pic.lib()
     for n in names:
         assert hasattr(h, n), n
@@ -73,5 +73,6 @@ def test_entry_points_reject_null_context():
     assert h.qc_score_select(None, C.byref(pool), C.byref(req), C.byref(qs), None, C.byref(sp), 0, None, None,
                              None, 0, None) == 1
     assert h.kv_fuse_scatter(None, C.byref(pool), C.byref(req), None, None, None, None, 0, 0, None) == 1
+    assert h.qc_anchor_select(None, C.byref(pool), C.byref(req), C.byref(sp), 0, None, None, None, 0, None) == 1
     n = C.c_size_t()
     assert h.pic_workspace_bytes(None, 0, C.byref(req), 0, 0, C.byref(n)) == 1

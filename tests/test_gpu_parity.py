@@ -319,6 +319,61 @@ def test_fuse_full_size_with_seeded_selection():
     assert np.max(np.abs(lse2.cpu().numpy()[ts, hs] - refl2)) <= LSE_ABS
 
 
+# ------------------------------------------------------- anchor extraction
+
+ANCHOR_RATIO = 0.05   # the pages call it a small fraction; declared, not given
+
+
+def _anchors(ctx, w, dc, ratio):
+    sel_off = pic.pic_select_offsets(w.span_len, ratio)
+    dc.span_req, dc.span_start, dc.span_len = H.dev(w.span_req), H.dev(w.span_start), H.dev(w.span_len)
+    dc.sel_off, dc.n_spans = H.dev(sel_off), len(w.span_req)
+    nsel = int(sel_off[-1])
+    sel = torch.full((max(nsel, 1),), -7, dtype=torch.int32, device=H.DEV)
+    norm = torch.full(w.kv_pos.shape, -1.0, dtype=torch.float32, device=H.DEV)
+    pic.qc_anchor_select(ctx, dc, nsel, sel, norm)
+    torch.cuda.synchronize()
+    return sel_off, sel.cpu().numpy()[:nsel], norm.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama_layer", "shared_small", "edge_spans", "long_spans"])
+def test_anchor_parity(name):
+    """Squared key norms within the fp32 accumulation bound of the oracle's,
+    and the anchors are the oracle's up to that band at the k-th boundary."""
+    w = small_select_workloads()[name]()
+    w.kv_pos[0, 5:9] = -1                         # masked slots score 0, never anchors
+    ctx = H.ctx_for(w)
+    dc = pic.to_device(w, H.DEV)
+    off, idx, norm = _anchors(ctx, w, dc, ANCHOR_RATIO)
+    ref = oracle.key_norm(w)
+    # bf16 squares are exact in fp32; the n = Hkv*d additions each round by at
+    # most one unit in the last place of the partial sum
+    rel = w.num_kv_heads * w.head_dim * 2.0 ** -24
+    for r in range(w.batch):
+        n = int(w.kv_len[r])
+        assert np.all(np.abs(norm[r, :n] - ref[r, :n]) <= rel * ref[r, :n]), r
+    ref_off, ref_idx = oracle.select(w, ref, ratio=ANCHOR_RATIO)
+    band = rel * float(ref.max())
+    check_selection(off, idx, ref_off, ref_idx, ref, w, band=band)
+    req0 = np.concatenate([idx[off[s]:off[s + 1]] for s in range(len(w.span_req)) if w.span_req[s] == 0])
+    assert not set(range(5, 9)) & set(req0.tolist())
+
+
+def test_anchor_full_size_and_bitwise_repeatable():
+    w = W.long_context()
+    ctx = H.ctx_for(w)
+    dc = pic.to_device(w, H.DEV)
+    off, idx, norm = _anchors(ctx, w, dc, ANCHOR_RATIO)
+    off2, idx2, norm2 = _anchors(ctx, w, dc, ANCHOR_RATIO)
+    assert np.array_equal(norm, norm2) and np.array_equal(idx, idx2)
+    ref = oracle.key_norm(w)
+    n = int(w.kv_len[0])
+    rel = w.num_kv_heads * w.head_dim * 2.0 ** -24
+    assert np.all(np.abs(norm[0, :n] - ref[0, :n]) <= rel * ref[0, :n])
+    ref_off, ref_idx = oracle.select(w, ref, ratio=ANCHOR_RATIO)
+    check_selection(off, idx, ref_off, ref_idx, ref, w, band=rel * float(ref.max()))
+
+
 # ------------------------------------------------------- sparse recompute
 
 def _recompute_case(w, sel_idx, req_off, seed):
