@@ -159,6 +159,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-recompute", action="store_true")
     ap.add_argument("--no-anchor", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--decode-private", action="store_true",
                     help="decode line on the unshared control (4 GiB pool)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -278,6 +279,38 @@ def main():
                          "step": "prefill+lse, qc_score_select, kv_fuse_scatter, prefill(fused), decode(1)"},
               "roofline": roofline, "ops_ms": {k: round(v, 5) for k, v in op_ms.items()}}
 
+    def time_calls(fn, reps=10, warm=2):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    ablation = None
+    if not args.no_ablation:
+        # Rotation-overhead ablation (MiniPIC reports 5.7% end to end): the same
+        # prefill call with keys_prerotated = 1, i.e. the keys used as stored.  It
+        # runs on the same pool bytes: the kernels' work does not depend on the
+        # key values.
+        dc.kv_pos.copy_(kv_pos0)
+        dc.kv_len.copy_(kv_len0)
+        dc.max_kv_len = kv0
+        ctx_pr = pic.Context(w.num_q_heads, w.num_kv_heads, w.head_dim, w.rope_theta, w.max_position,
+                             keys_prerotated=True)
+        t_rot = time_calls(lambda: pic.pic_attn_prefill(ctx, dc, out1, lse1, ws=ws, stream=stream))
+        t_pre = time_calls(lambda: pic.pic_attn_prefill(ctx_pr, dc, out1, lse1, ws=ws, stream=stream))
+        ctx_pr.close()
+        ablation = {"what": "same kernels with keys stored rotated (keys_prerotated = 1) vs rotated in-kernel "
+                            "at each key's logical position; timed on the same bytes",
+                    "prefill_step1_ms": {"in_kernel": round(t_rot, 5), "prerotated": round(t_pre, 5),
+                                         "overhead": round(t_rot / t_pre - 1.0, 4)}}
+        result["rotation_ablation"] = ablation
+
     if not args.no_recompute:
         # Discrete-token recompute (QCFuse's sparse recompute): the 4,928 selected
         # tokens as queries at their own logical positions over the fused cache.
@@ -368,6 +401,14 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         dms = e0.elapsed_time(e1) / reps
+        if ablation is not None:
+            ctxd_pr = pic.Context(wd.num_q_heads, wd.num_kv_heads, wd.head_dim, wd.rope_theta, wd.max_position,
+                                  keys_prerotated=True)
+            d_pre = time_calls(lambda: pic.pic_attn_decode(ctxd_pr, dd, dd.q, dd.q_pos, outd, None, ws=wsd,
+                                                           stream=stream), reps=20, warm=3)
+            ctxd_pr.close()
+            ablation["decode_heavy_ms"] = {"in_kernel": round(dms, 5), "prerotated": round(d_pre, 5),
+                                           "overhead": round(dms / d_pre - 1.0, 4)}
         dtok = attended_tokens(wd)
         kvbytes = dtok * wd.num_kv_heads * wd.head_dim * 2 * 2
         result["decode_heavy"] = {

@@ -74,6 +74,12 @@ typedef struct {
     int32_t block_size;     /* must be PIC_BLOCK_SIZE */
     int32_t max_position;   /* rows of the cos/sin table, 1 .. 1<<22 */
     double rope_theta;      /* > 0 */
+    /* 0 (the method): the pool holds unrotated keys, rotated in-kernel at each
+     * key's per-request logical position.  1 (ablation of that rotation, the
+     * standard RoPE cache): every key is stored already rotated at its
+     * position and used as stored; queries are still rotated at q_pos.  Only
+     * valid when no block serves two different positions for one slot. */
+    int32_t keys_prerotated;
 } pic_config;
 
 typedef struct pic_ctx pic_ctx;

@@ -192,6 +192,7 @@ void fill_fwd_common(pic::FwdParams &p, const pic_ctx *ctx, const pic_kv_pool *p
     p.group = c.num_q_heads / c.num_kv_heads;
     p.cos_tab = ctx->cos_d;
     p.sin_tab = ctx->sin_d;
+    p.rotate_k = c.keys_prerotated ? 0 : 1;
     p.max_pos = c.max_position;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
     p.max_kv_len = req->max_kv_len;
@@ -228,6 +229,7 @@ pic_status pic_ctx_create(const pic_config *cfg, pic_ctx **out) {
     if (!(cfg->rope_theta > 0.0) || !std::isfinite(cfg->rope_theta)) return PIC_ERR_INVALID_ARG;
     if (cfg->head_dim != 64 && cfg->head_dim != 128) return PIC_ERR_UNSUPPORTED;
     if (cfg->block_size != PIC_BLOCK_SIZE) return PIC_ERR_UNSUPPORTED;
+    if (cfg->keys_prerotated != 0 && cfg->keys_prerotated != 1) return PIC_ERR_INVALID_ARG;
 
     pic_ctx *ctx = new (std::nothrow) pic_ctx;
     if (!ctx) return PIC_ERR_HIP;
@@ -387,6 +389,7 @@ pic_status pic_attn_decode(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
     p.group = c.num_q_heads / c.num_kv_heads;
     p.cos_tab = ctx->cos_d;
     p.sin_tab = ctx->sin_d;
+    p.rotate_k = c.keys_prerotated ? 0 : 1;
     p.max_pos = c.max_position;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
     p.max_kv_len = req->max_kv_len;

@@ -196,13 +196,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 cc = cp * cd - sn * sd;
                 ss = sn * cd + cp * sd;
             };
+            if (p.rotate_k) {   // else the keys are stored rotated (ablation mode)
 #pragma unroll
-            for (int c = 0; c < NC / 2; ++c) {
-                f32x4 c0, s0, c1, s1;
-                rot(32 * c + 8 * lg, c0, s0);
-                rot(32 * c + 8 * lg + 4, c1, s1);
-                rope4<0>(cur.k[T][c], cur.k[T][c + NC / 2], c0, s0);
-                rope4<1>(cur.k[T][c], cur.k[T][c + NC / 2], c1, s1);
+                for (int c = 0; c < NC / 2; ++c) {
+                    f32x4 c0, s0, c1, s1;
+                    rot(32 * c + 8 * lg, c0, s0);
+                    rot(32 * c + 8 * lg + 4, c1, s1);
+                    rope4<0>(cur.k[T][c], cur.k[T][c + NC / 2], c0, s0);
+                    rope4<1>(cur.k[T][c], cur.k[T][c + NC / 2], c1, s1);
+                }
             }
 #pragma unroll
             for (int c = 0; c < NC; ++c) sacc[T] = mfma16(cur.k[T][c], qop[c], sacc[T]);

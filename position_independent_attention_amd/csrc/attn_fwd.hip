@@ -252,6 +252,7 @@ __device__ __forceinline__ void data_load(const FwdParams &p, Data<D, WAVES> &dt
 template <int D, int WAVES>
 __device__ __forceinline__ void cs_load(const FwdParams &p, Data<D, WAVES> &dt, int tid) {
     using GG = Geo<D, WAVES>;
+    if (!p.rotate_k) return;   // keys stored rotated: no table rows
 #pragma unroll
     for (int u = 0; u < GG::KTASK; ++u) {
         const int pc = tid % GG::PC;
@@ -269,7 +270,7 @@ __device__ __forceinline__ void cs_load(const FwdParams &p, Data<D, WAVES> &dt, 
 // this thread staged is usable and visible to the workgroup's earliest row.
 template <int D, int WAVES>
 __device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uint16_t *Vs, int32_t *s_pi, int tid,
-                                           bool need_v, int min_pos) {
+                                           bool need_v, int min_pos, bool rot) {
     using GG = Geo<D, WAVES>;
     bool full = true;
 #pragma unroll
@@ -278,7 +279,7 @@ __device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uin
         const int pc = tid % GG::PC;
         const int pi = dt.kpi[u];
         u32x4 lo = dt.klo[u], hi = dt.khi[u];
-        rope8(lo, hi, dt.cs[u][0], dt.cs[u][1], dt.cs[u][2], dt.cs[u][3]);
+        if (rot) rope8(lo, hi, dt.cs[u][0], dt.cs[u][1], dt.cs[u][2], dt.cs[u][3]);
         const int kr = krow(kk);
         *reinterpret_cast<u32x4 *>(Ks + koff<D>(kr, pc)) = lo;
         *reinterpret_cast<u32x4 *>(Ks + koff<D>(kr, GG::PC + pc)) = hi;
@@ -449,7 +450,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     __syncthreads();
     const int first_bad = s_firstbad;
     if (ntiles > 0) {
-        (void)data_store<D, WAVES>(dnext, Ks, Vs, s_pi, tid, kV, min_pos);
+        (void)data_store<D, WAVES>(dnext, Ks, Vs, s_pi, tid, kV, min_pos, p.rotate_k != 0);
         __syncthreads();
     }
     const float sc = p.scale_log2;
@@ -658,7 +659,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         bool f = true;
         if constexpr (MORE)
             f = data_store<D, WAVES>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs + (kV ? (cur ^ 1) * GG::VBUF : 0),
-                                     s_pi + (cur ^ 1) * kTileN, tid, kV, min_pos);
+                                     s_pi + (cur ^ 1) * kTileN, tid, kV, min_pos, p.rotate_k != 0);
         if constexpr (MODE != kMass) {
             interleave_hint<QG * (D / 16 + 1), 3>();
             commit(mn1);
@@ -871,7 +872,7 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
     __syncthreads();
     const int first_bad = s_firstbad;
     if (ntiles > 0) {
-        (void)data_store<D, WAVES>(dnext, Ks, Vs, s_pi, tid, false, min_pos);
+        (void)data_store<D, WAVES>(dnext, Ks, Vs, s_pi, tid, false, min_pos, p.rotate_k != 0);
         __syncthreads();
         data_load<D, WAVES>(p, dnext, m2, g, key_begin + kTileN, key_end, tid, false);
         meta_load<D, WAVES>(m2, bt, pis, key_begin + 2 * kTileN, key_end, tid);
@@ -942,7 +943,7 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
         }
         if constexpr (MORE)
             (void)data_store<D, WAVES>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs, s_pi + (cur ^ 1) * kTileN, tid, false,
-                                       min_pos);
+                                       min_pos, p.rotate_k != 0);
         __syncthreads();
         if (tid < kTileN) {
             float tot = 0.f;

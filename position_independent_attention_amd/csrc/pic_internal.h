@@ -32,6 +32,7 @@ struct FwdParams {
     int32_t hq, hkv, group;
     const float *cos_tab;     // [max_pos][d/2]
     const float *sin_tab;
+    int32_t rotate_k;         // 0: keys are stored rotated (ablation mode)
     int32_t max_pos;
     float scale_log2;         // log2(e) / sqrt(d)
     int32_t max_kv_len;       // host bound on kv_len (clamps every key range)
@@ -64,6 +65,7 @@ struct DecodeParams {
     int32_t hq, hkv, group;
     const float *cos_tab;
     const float *sin_tab;
+    int32_t rotate_k;         // 0: keys are stored rotated (ablation mode)
     int32_t max_pos;
     float scale_log2;
     int32_t max_kv_len;

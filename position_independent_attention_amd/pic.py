@@ -30,7 +30,8 @@ _i32 = C.c_int32
 
 class PicConfig(C.Structure):
     _fields_ = [("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
-                ("block_size", _i32), ("max_position", _i32), ("rope_theta", C.c_double)]
+                ("block_size", _i32), ("max_position", _i32), ("rope_theta", C.c_double),
+                ("keys_prerotated", _i32)]
 
 
 class PicKvPool(C.Structure):
@@ -116,8 +117,9 @@ class Context:
     """pic_ctx_create / pic_ctx_destroy.  Create it with the target device current."""
 
     def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, rope_theta: float,
-                 max_position: int = 65536, block_size: int = PIC_BLOCK_SIZE):
-        self.cfg = PicConfig(num_q_heads, num_kv_heads, head_dim, block_size, max_position, rope_theta)
+                 max_position: int = 65536, block_size: int = PIC_BLOCK_SIZE, keys_prerotated: bool = False):
+        self.cfg = PicConfig(num_q_heads, num_kv_heads, head_dim, block_size, max_position, rope_theta,
+                             1 if keys_prerotated else 0)
         h = _vp()
         st = lib().pic_ctx_create(C.byref(self.cfg), C.byref(h))
         if st != PIC_OK:

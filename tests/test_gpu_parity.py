@@ -374,6 +374,58 @@ def test_anchor_full_size_and_bitwise_repeatable():
     check_selection(off, idx, ref_off, ref_idx, ref, w, band=rel * float(ref.max()))
 
 
+# ------------------------------------------------ pre-rotated keys (ablation)
+
+def _prerotated(w):
+    """Copy of w whose K pool holds every usable slot's key rotated at its pi by
+    the oracle's rope, rounded to bf16: the standard RoPE cache that the
+    keys_prerotated mode reads.  Fails if a slot would need two positions
+    (a block shared at different offsets cannot be pre-rotated)."""
+    wp = w.copy()
+    seen = {}
+    for r in range(w.batch):
+        for j in range(int(w.kv_len[r])):
+            pi, blk = int(w.kv_pos[r, j]), int(w.block_table[r, j // 16])
+            if pi < 0 or blk < 0:
+                continue
+            assert seen.setdefault((blk, j % 16), pi) == pi, "slot needed at two positions"
+            if (blk, j % 16, "done") in seen:
+                continue
+            seen[(blk, j % 16, "done")] = True
+            for g in range(w.num_kv_heads):
+                k = W.bf16_bits_to_f32(w.pool_k[blk, g, j % 16]).astype(np.float64)
+                kr = oracle.rope(w.head_dim, w.rope_theta, pi, k)
+                wp.pool_k[blk, g, j % 16] = W.f32_to_bf16_bits(kr.astype(np.float32))
+    return wp
+
+
+def test_prerotated_mode_prefill_and_mass():
+    """Ablation of the in-kernel rotation: keys stored rotated, used as stored;
+    results equal the method's (the oracle on the unrotated cache)."""
+    w = W.long_context(n_spans=4, span_tok=512, q_len=64)
+    wp = _prerotated(w)
+    ctx = pic.Context(w.num_q_heads, w.num_kv_heads, w.head_dim, w.rope_theta, w.max_position,
+                      keys_prerotated=True)
+    out, lse, dc = H.prefill(ctx, wp)
+    ref_o, ref_l = oracle.attention(w)
+    compare_out(H.host_bf16(out), ref_o, "O prerotated")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+    _, _, mass = H.select(ctx, wp, dc, lse)
+    n = int(w.kv_len[0])
+    assert mass_within(mass[0, :n], oracle.mass(w)[0, :n])
+
+
+def test_prerotated_mode_decode():
+    w = W.decode_heavy(batch=3, n_spans=2, span_tok=512, private_spans=True, Hq=32)
+    wp = _prerotated(w)
+    ctx = pic.Context(w.num_q_heads, w.num_kv_heads, w.head_dim, w.rope_theta, w.max_position,
+                      keys_prerotated=True)
+    out, lse, _ = H.decode(ctx, wp)
+    ref_o, ref_l = oracle.attention(w)
+    compare_out(H.host_bf16(out), ref_o, "O prerotated decode")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+
+
 # ------------------------------------------------------- sparse recompute
 
 def _recompute_case(w, sel_idx, req_off, seed):
