@@ -160,6 +160,7 @@ def main():
     ap.add_argument("--no-recompute", action="store_true")
     ap.add_argument("--no-anchor", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--no-hashing", action="store_true")
     ap.add_argument("--decode-private", action="store_true",
                     help="decode line on the unshared control (4 GiB pool)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -421,6 +422,37 @@ def main():
                          "algorithmic_bytes": kvbytes}}
         del dd, outd, wsd
         ctxd.close()
+
+    if not args.no_hashing:
+        # Span reuse by block hashing (host): 64 requests, each a private prompt
+        # and 16 SSEP spans of 1,024 tokens drawn from a pool of 64 spans.
+        rng = np.random.default_rng(11)
+        bs = pic.PIC_BLOCK_SIZE
+        pool_sp = []
+        for _ in range(64):
+            sp = [1] + rng.integers(10, 50000, 1024).tolist()
+            pool_sp.append(sp + [-1] * ((-len(sp)) % bs))
+        reqs = []
+        for _ in range(64):
+            pr = rng.integers(10, 50000, int(rng.integers(16, 200))).tolist()
+            t = pr + [-1] * ((-len(pr)) % bs)
+            for k in rng.integers(0, 64, 16):
+                t += pool_sp[int(k)]
+            reqs.append(np.asarray(t, np.int32))
+        ntok = sum(len(t) for t in reqs)
+        cache = pic.BlockCache(200000)
+        c0 = time.perf_counter()
+        misses = blocks = 0
+        for t in reqs:
+            _, _, m = cache.map_request(t, -1, 1, 2)
+            misses += int(m.sum())
+            blocks += len(m)
+        hsec = time.perf_counter() - c0
+        cache.close()
+        result["block_hashing"] = {
+            "workload": f"64 requests, {ntok} tokens: private prompts + 16 SSEP spans of 1,024 tokens each from a "
+                        "pool of 64", "host_ms": round(hsec * 1e3, 3), "tokens_per_s": round(ntok / hsec, 1),
+            "blocks": blocks, "reused_blocks": blocks - misses, "where": "host CPU (pic_block_map)"}
 
     if not args.no_cpu_baseline:
         import oracle

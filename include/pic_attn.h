@@ -241,6 +241,40 @@ pic_status kv_fuse_scatter(pic_ctx *ctx, pic_kv_pool *pool, pic_req_table *req,
                            const uint16_t *k_new, const uint16_t *v_new, int32_t n_sel,
                            int32_t max_rows_per_req, void *stream);
 
+/* ---- Span reuse by block hashing ([MiniPIC] section 2.2: padding, SSEP and
+ * PDEP special tokens change how KV blocks are hashed).  Host code; no GPU.
+ *
+ * A block cache maps block hashes to physical pool block ids 0..num_blocks-1.
+ * pic_block_map turns one request's token stream (host memory) into its block
+ * table and per-slot logical positions:
+ *   - a block's hash chains on its predecessor's;
+ *   - a block whose first token is ssep_token restarts the chain from the
+ *     root, so the span is cached independently of what precedes it and is
+ *     reused at any offset;
+ *   - a block whose first token is pdep_token takes the unbroken chain over
+ *     the whole prompt so far, so it only matches an identical prompt;
+ *   - H is 64-bit FNV-1a over the parent hash (8 bytes, little-endian) and
+ *     the block's 16 token ids (4 bytes each, little-endian), rooted at the
+ *     FNV offset basis.  Only full blocks are cacheable.
+ * Outputs (host int32):
+ *   block_table [max_blocks]: physical block of each of the request's blocks;
+ *   miss [max_blocks]: 1 when the block was newly taken (its K/V must be
+ *     computed and stored by the caller), 0 when an equal block is reused;
+ *   kv_pos [max_blocks * 16]: logical position of each slot, counting non-PAD
+ *     tokens; -1 for PAD slots and past n_tokens;
+ *   n_blocks = ceil(n_tokens / 16).
+ * A miss takes the lowest free block id.  PIC_ERR_WORKSPACE (and nothing
+ * changed) when the cache has fewer free blocks than the request needs;
+ * PIC_ERR_INVALID_ARG for NULL pointers, negative sizes or max_blocks too
+ * small.  Blocks are never released (no eviction).  Not thread-safe per
+ * cache. */
+typedef struct pic_block_cache pic_block_cache;
+pic_status pic_block_cache_create(int32_t num_blocks, pic_block_cache **out);
+void pic_block_cache_destroy(pic_block_cache *cache);
+pic_status pic_block_map(pic_block_cache *cache, const int32_t *tokens, int32_t n_tokens, int32_t pad_token,
+                         int32_t ssep_token, int32_t pdep_token, int32_t *block_table, int32_t max_blocks,
+                         int32_t *kv_pos, int32_t *miss, int32_t *n_blocks);
+
 #ifdef __cplusplus
 }
 #endif

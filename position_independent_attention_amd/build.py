@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpicattn.so")
-SOURCES = ["attn_fwd.hip", "attn_decode.hip", "select_fuse.hip", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_decode.hip", "select_fuse.hip", "api.cpp", "block_hash.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -94,6 +94,12 @@ def lib() -> C.CDLL:
         h.qc_anchor_select.argtypes = [_vp, P(PicKvPool), P(PicReqTable), P(PicSpans), _i32, _vp, _vp, _vp,
                                        C.c_size_t, _vp]
         h.qc_anchor_select.restype = C.c_int
+        h.pic_block_cache_create.argtypes = [_i32, P(_vp)]
+        h.pic_block_cache_create.restype = C.c_int
+        h.pic_block_cache_destroy.argtypes = [_vp]
+        h.pic_block_cache_destroy.restype = None
+        h.pic_block_map.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, P(_i32)]
+        h.pic_block_map.restype = C.c_int
         h.kv_fuse_scatter.argtypes = [_vp, P(PicKvPool), P(PicReqTable), _vp, _vp, _vp, _vp, _i32, _i32, _vp]
         h.kv_fuse_scatter.restype = C.c_int
         _lib = h
@@ -277,3 +283,41 @@ def kv_fuse_scatter(ctx: Context, dc: DeviceCache, sel_idx, sel_req_off, k_new, 
     st = lib().kv_fuse_scatter(ctx.handle, C.byref(pool), C.byref(req), _ptr(sel_idx), _ptr(sel_req_off),
                                _ptr(k_new), _ptr(v_new), int(n_sel), int(max_rows_per_req), _stream(stream))
     _check(ctx, st, "kv_fuse_scatter")
+
+
+class BlockCache:
+    """pic_block_cache_*: span reuse by block hashing (host only)."""
+
+    def __init__(self, num_blocks: int):
+        h = _vp()
+        st = lib().pic_block_cache_create(int(num_blocks), C.byref(h))
+        if st != PIC_OK:
+            raise PicError(st, "pic_block_cache_create")
+        self.handle = h
+
+    def map_request(self, tokens, pad_token: int, ssep_token: int, pdep_token: int):
+        """(block_table, kv_pos[:n_tokens], miss) as numpy int32 arrays."""
+        import numpy as np
+        t = np.ascontiguousarray(tokens, np.int32)
+        nb = (t.shape[0] + PIC_BLOCK_SIZE - 1) // PIC_BLOCK_SIZE
+        table = np.zeros(max(nb, 1), np.int32)
+        miss = np.zeros(max(nb, 1), np.int32)
+        pos = np.zeros(max(nb, 1) * PIC_BLOCK_SIZE, np.int32)
+        n = _i32()
+        st = lib().pic_block_map(self.handle, t.ctypes.data_as(_vp), int(t.shape[0]), int(pad_token),
+                                 int(ssep_token), int(pdep_token), table.ctypes.data_as(_vp), int(nb),
+                                 pos.ctypes.data_as(_vp), miss.ctypes.data_as(_vp), C.byref(n))
+        if st != PIC_OK:
+            raise PicError(st, "pic_block_map")
+        return table[:n.value], pos[:t.shape[0]], miss[:n.value]
+
+    def close(self):
+        if self.handle:
+            lib().pic_block_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -6,6 +6,7 @@ a 1e-3 band around each span's k-th mass (ties to the lower index); fusion
 bit-exact.  Small shapes compare every output; the full-size shapes compare
 sampled rows and size-independent properties.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -469,6 +470,62 @@ def test_recompute_full_size_sampled():
     ref_o, ref_l = oracle.attention(wr, (ts, hs))
     compare_out(H.host_bf16(out)[ts, hs], ref_o, "O recompute sampled")
     assert np.max(np.abs(lse.cpu().numpy()[ts, hs] - ref_l)) <= LSE_ABS
+
+
+# ------------------------------------------- span reuse by block hashing
+
+def test_block_hash_reuse_end_to_end():
+    """Token streams with the same SSEP spans at different offsets: the block
+    cache hands both requests the same physical blocks, K/V are written only
+    for missed blocks, and attention over the shared pool equals the oracle
+    and equals private copies bit for bit."""
+    from tests.test_block_hash import PAD, SSEP, PDEP, padded, span
+    sp = [padded(span(200 + i, 60 + 37 * i), SSEP) for i in range(3)]
+    streams = [padded(span(300, 20)) + sp[0] + sp[1] + sp[2],
+               padded(span(301, 70)) + sp[2] + sp[0] + padded(span(302, 5), PDEP)]
+    Hq, Hkv, d = 8, 2, 64
+    nb_pool = 64
+    cache = pic.BlockCache(nb_pool)
+    maps = [cache.map_request(np.asarray(t, np.int32), PAD, SSEP, PDEP) for t in streams]
+    cache.close()
+    assert sum(int(m[2].sum()) for m in maps) < sum(len(m[0]) for m in maps)   # something was reused
+    rng = np.random.default_rng(303)
+    pool_k = np.zeros((nb_pool, Hkv, 16, d), np.uint16)
+    pool_v = np.zeros((nb_pool, Hkv, d, 16), np.uint16)
+    for table, _, miss in maps:
+        for b, m in zip(table, miss):
+            if m:   # the caller computes K/V of a missed block once
+                pool_k[b] = W.f32_to_bf16_bits(rng.standard_normal((Hkv, 16, d), dtype=np.float32))
+                pool_v[b] = W.f32_to_bf16_bits(rng.standard_normal((Hkv, d, 16), dtype=np.float32))
+    maxb = max(len(m[0]) for m in maps)
+    bt = np.full((2, maxb), -1, np.int32)
+    kvp = np.full((2, maxb * 16), -1, np.int32)
+    kvl = np.zeros(2, np.int32)
+    for r, (table, pos, _) in enumerate(maps):
+        bt[r, :len(table)] = table
+        kvp[r, :len(pos)] = pos
+        kvl[r] = len(pos)
+    q_len = 6
+    q_pos = np.concatenate([np.arange(q_len) + int(kvp[r].max()) + 1 for r in range(2)]).astype(np.int32)
+    w = dataclasses.replace(W.tiny(), name="block_hash", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                            rope_theta=1e4, batch=2, pool_k=pool_k, pool_v=pool_v, block_table=bt,
+                            kv_len=kvl, kv_pos=kvp,
+                            q=W.fresh_queries(2 * q_len, Hq, d, seed=304),
+                            q_start=np.array([0, q_len, 2 * q_len], np.int32), q_pos=q_pos)
+    ctx = H.ctx_for(w)
+    out, lse, _ = H.prefill(ctx, w)
+    ref_o, ref_l = oracle.attention(w)
+    compare_out(H.host_bf16(out), ref_o, "O block-hash reuse")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+    # private copies of request 1's blocks give the same bits
+    wp = w.copy()
+    n1 = len(maps[1][0])
+    fresh_ids = np.arange(nb_pool - n1, nb_pool)
+    wp.pool_k[fresh_ids] = w.pool_k[bt[1, :n1]]
+    wp.pool_v[fresh_ids] = w.pool_v[bt[1, :n1]]
+    wp.block_table[1, :n1] = fresh_ids
+    out2, _, _ = H.prefill(ctx, wp)
+    assert np.array_equal(out.cpu().numpy(), out2.cpu().numpy())
 
 
 # ------------------------------------------------------- sharing / repeat
