@@ -4,19 +4,24 @@
 //
 // Bound by HBM bytes: every cached key and value is read once per
 // (request, kv head) and feeds only G = Hq/Hkv query rows.  So there is no
-// LDS staging of K/V: each wave streams its own 32-key steps straight from
-// global memory into MFMA operand registers (the next step's K, V and
-// positions are requested before the current step's math), rotates the K
-// operand in registers, and runs the same transposed S^T = K Q^T /
-// O^T += V^T P^T scheme as the prefill kernel (the G query heads are the MFMA
-// columns; columns >= G are masked).
+// LDS staging of K/V: each wave walks its range one pool block (16 keys) at a
+// time, loading the block's keys and values straight into MFMA operand
+// registers.  Scores are S^T = K Q^T (16x16x32 bf16, the G query heads are
+// the MFMA columns, columns >= G are masked); the S^T accumulator layout is
+// exactly the B operand of the 16x16x16 bf16 MFMA, so O^T += V^T P^T takes
+// the probabilities without any data movement, and V^T comes 8 bytes per
+// lane from the block's channel-major value layout.
 //
-// Rotation of key j at position pi uses R(pi) = R(pi - dl) R(dl) with dl the
-// key's offset inside its 16-key block (capped at pi): the keys of a block
-// that holds consecutive positions then all read the one table row pi - dl,
-// which stays in L1, and R(dl) for dl = 0..15 (rows 0..15 of the same table)
-// sits in LDS.  Any dl in 0..pi gives the same rotation, so blocks holding
-// arbitrary positions are handled by the same code.
+// Rotation of key j at position pi: when the usable keys of a block sit at
+// pi = base + offset (the usual case, also for a span reused at another
+// offset), R(pi) = R(base) R(offset); the block's base cos/sin row (512 bytes
+// at d = 128) is requested with the block and passed through LDS, and R(o)
+// for o = 0..15 sits in LDS for the whole kernel.  Any other block reads each
+// key's own table row.  Positions are requested two blocks ahead, so a
+// block's path and base row are known when its keys are requested, and every
+// load of a block is issued before the previous block's math (memory
+// requests retire in order, so a load issued later would also wait for the
+// prefetch).
 //
 // A workgroup (4 waves) covers split_len keys of one (request, kv head);
 // waves are merged through LDS and splits by the LSE merge kernel.
@@ -30,6 +35,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -41,6 +49,11 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                     0, 0, 0);
+}
+constexpr float kSlack = 8.f;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Rotate 4 RoPE pairs: words 2*hh, 2*hh+1 of lo hold x[i..i+3] (first
@@ -64,57 +77,77 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
     return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
 }
 
-// One 32-key step's operands for one lane (cos/sin are fetched at use).
+// Positions of one 16-key step (one pool block), requested two steps ahead.
+struct Pos {
+    i32x4 a;        // pi of keys 4lg .. 4lg+3 (raw)
+    int32_t x;      // pi of key lc (raw)
+    int32_t blk;    // pool block id (raw, uniform)
+};
+
+// One 16-key step's operands for one lane, requested one step ahead.
 template <int D>
 struct Step {
     static constexpr int NC = D / 32;
-    u32x4 k[2][NC];      // A operand rows (before rotation), tiles T = 0, 1
-    int32_t kpi[2];      // pi of the A row keys (-1 unusable)
-    u32x4 v[D / 16];     // V^T operand, channel 16*dt + lc, keys 8lg..8lg+7
-    int32_t spi[8];      // pi of this lane's 8 score keys (-1 unusable)
+    u32x4 k[NC];        // S^T A operand: key lc, channels 32c + 8lg .. +7 (before rotation)
+    u32x2 v[D / 16];    // O^T A operand: channel 16dt + lc, keys 4lg .. 4lg+3
+    f32x2 row;          // two entries of the cos (lanes of even half-groups) or sin row at the block base
+    int32_t spi[4];     // pi of keys 4lg .. 4lg+3 (-1 unusable)
+    int32_t kpi;        // pi of key lc (-1 unusable)
+    int32_t fast;       // every usable key of the block sits at pi = base + offset
 };
 
-// Unconditional loads at clamped indices (key_end >= 1; kv_stride, a multiple
-// of 16, bounds every index), then selects: unusable keys read the zero page.
+// kb is a multiple of 16 and wave-uniform; lastb = (key_end - 1) & ~15 bounds
+// every index (kv_stride is a multiple of 16), so the loads need no branch.
+__device__ __forceinline__ void pos_load(Pos &q, const int32_t *bt, const int32_t *pis, int kb, int lastb, int lc,
+                                         int lg) {
+    const int kbc = min(kb, lastb);
+    q.a = *reinterpret_cast<const i32x4 *>(pis + kbc + 4 * lg);
+    q.x = pis[kbc + lc];
+    q.blk = bt[kbc >> 4];
+}
+
+// Validate a step's positions, pick its rotation path and request its K, V
+// and base cos/sin row.  Unusable blocks read the zero page.
 template <int D>
-__device__ __forceinline__ void step_load(const DecodeParams &p, Step<D> &st, const int32_t *bt,
-                                          const int32_t *pis, int g, int kb, int key_end, int lc, int lg) {
-    constexpr int NC = D / 32;
-    const int last = key_end - 1;
+__device__ __forceinline__ void step_issue(const DecodeParams &p, Step<D> &st, const Pos &q, int g, int kb,
+                                           int key_end, int lane, int lc, int lg) {
+    constexpr int NC = D / 32, HALF = D / 2;
+    const int blk = __builtin_amdgcn_readfirstlane(q.blk);
+    const bool bok = (unsigned)blk < (unsigned)p.num_blocks;
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
-        const int j = kb + 8 * (lc >> 2) + 4 * T + (lc & 3);
-        const int jc = min(j, last);
-        const int blk = bt[jc >> 4], pi = pis[jc];
-        const bool ok = j < key_end && (unsigned)blk < (unsigned)p.num_blocks && (unsigned)pi < (unsigned)p.max_pos;
-        st.kpi[T] = ok ? pi : -1;
-        const uint16_t *row = ok ? p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + (j & 15)) * D : p.zero_page;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) st.k[T][c] = *reinterpret_cast<const u32x4 *>(row + 32 * c + 8 * lg);
+    for (int i = 0; i < 4; ++i)
+        st.spi[i] = (bok && kb + 4 * lg + i < key_end && (unsigned)q.a[i] < (unsigned)p.max_pos) ? q.a[i] : -1;
+    st.kpi = (bok && kb + lc < key_end && (unsigned)q.x < (unsigned)p.max_pos) ? q.x : -1;
+    // base = pi - offset, the same for every usable key of the block?
+    const bool use = st.kpi >= 0;
+    const int cand = st.kpi - lc;
+    const uint64_t um = __ballot(use);
+    int base = 0, fast = 1;
+    if (um) {
+        base = __builtin_amdgcn_readlane(cand, (int)__builtin_ctzll(um));
+        fast = base >= 0 && __ballot(use && cand != base) == 0;
     }
-    const int j0 = kb + 8 * lg;                 // multiple of 8
-    const int j0c = min(j0, last & ~7);         // 8 positions from here stay inside the row
-    const int blk = bt[j0c >> 4];
-    const bool bok = j0 < key_end && (unsigned)blk < (unsigned)p.num_blocks;
-    const i32x4 a = *reinterpret_cast<const i32x4 *>(pis + j0c);
-    const i32x4 b = *reinterpret_cast<const i32x4 *>(pis + j0c + 4);
+    st.fast = fast;
+    const int rb = fast ? base : 0;
+    const float *tab = ((lane / (HALF / 2)) & 1) ? p.sin_tab : p.cos_tab;
+    st.row = *reinterpret_cast<const f32x2 *>(tab + (size_t)rb * HALF + 2 * (lane % (HALF / 2)));
+    const uint16_t *kr = bok ? p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + lc) * D : p.zero_page;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        st.spi[i] = (bok && j0 + i < key_end && (unsigned)a[i] < (unsigned)p.max_pos) ? a[i] : -1;
-        st.spi[4 + i] = (bok && j0 + 4 + i < key_end && (unsigned)b[i] < (unsigned)p.max_pos) ? b[i] : -1;
-    }
-    const uint16_t *vb = bok ? p.v_pool + ((size_t)blk * p.hkv + g) * D * kBlock + (j0 & 15) : p.zero_page;
+    for (int c = 0; c < NC; ++c) st.k[c] = *reinterpret_cast<const u32x4 *>(kr + 32 * c + 8 * lg);
+    const uint16_t *vb = bok ? p.v_pool + ((size_t)blk * p.hkv + g) * D * kBlock : p.zero_page;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-        st.v[dt] = *reinterpret_cast<const u32x4 *>(vb + (size_t)(16 * dt + lc) * kBlock);
+        st.v[dt] = *reinterpret_cast<const u32x2 *>(vb + (size_t)(16 * dt + lc) * kBlock + 4 * lg);
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeParams p) {
     constexpr int NC = D / 32, HALF = D / 2, NQ = HALF / 4;
-    // R(dl) for dl = 0..15, laid out [frequency quad][dl]: the 16 lanes of a
-    // lane group read one 256-byte block
+    // R(o) for block offsets o = 0..15, laid out [frequency quad][o]: the 16
+    // lanes of a lane group read one 256-byte block
     __shared__ f32x4 s_dc[NQ][16], s_ds[NQ][16];
+    // each wave's current block-base row: cos, then sin
+    __shared__ f32x4 s_row[kWaves][2][NQ];
     __shared__ float s_o[kWaves][D][16];
     __shared__ float s_m[kWaves][16], s_l[kWaves][16];
 
@@ -125,13 +158,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int sp = lid % p.num_splits;
     const int r = lid / p.num_splits;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lc = lane & 15, lg = lane >> 4;
     for (int t = tid; t < NQ * 16; t += kThreads) {
-        const int dl = t & 15, q4 = t >> 4;
-        const bool in = dl < p.max_pos;
-        s_dc[q4][dl] = in ? *reinterpret_cast<const f32x4 *>(p.cos_tab + dl * HALF + 4 * q4) : f32x4{1.f, 1.f, 1.f, 1.f};
-        s_ds[q4][dl] = in ? *reinterpret_cast<const f32x4 *>(p.sin_tab + dl * HALF + 4 * q4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const int o = t & 15, q4 = t >> 4;
+        const bool in = o < p.max_pos;
+        s_dc[q4][o] = in ? *reinterpret_cast<const f32x4 *>(p.cos_tab + o * HALF + 4 * q4) : f32x4{1.f, 1.f, 1.f, 1.f};
+        s_ds[q4][o] = in ? *reinterpret_cast<const f32x4 *>(p.sin_tab + o * HALF + 4 * q4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     const int kv_stride = p.max_blocks * kBlock;
@@ -169,99 +203,119 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     }
 
-    float m_run = -INFINITY, l_run = 0.f;
+    // running max: a per-column reference raised only when a score passes it
+    // by more than kSlack (log2 units), so most steps skip the rescale
+    float m_ref = -1e30f, l_run = 0.f;
     f32x4 acc[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    __syncthreads();   // R(dl) table
+    __syncthreads();   // R(o) table
 
-    // wave-uniform step count (the compiler cannot tell on its own)
-    const int nsteps = __builtin_amdgcn_readfirstlane(key_end > wbeg ? (key_end - wbeg + 31) / 32 : 0);
-    auto process = [&](Step<D> &cur) {
-        f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-            // key offset inside its block (the step start is a multiple of 32)
-            const int off = (8 * (lc >> 2) + 4 * T + (lc & 3)) & 15;
-            const int pi = cur.kpi[T];
-            const int dl = pi >= 0 ? min(off, pi) : 0;
-            const int row = pi >= 0 ? pi - dl : 0;
-            const float *cr = p.cos_tab + (size_t)row * HALF;
-            const float *sr = p.sin_tab + (size_t)row * HALF;
-            // cos/sin of 4 frequencies i0..i0+3 at pi: R(pi - dl) R(dl)
-            auto rot = [&](int i0, f32x4 &cc, f32x4 &ss) {
-                const f32x4 cp = *reinterpret_cast<const f32x4 *>(cr + i0);
-                const f32x4 sn = *reinterpret_cast<const f32x4 *>(sr + i0);
-                const f32x4 cd = s_dc[i0 >> 2][dl], sd = s_ds[i0 >> 2][dl];
-                cc = cp * cd - sn * sd;
-                ss = sn * cd + cp * sd;
-            };
-            if (p.rotate_k) {   // else the keys are stored rotated (ablation mode)
+    auto process = [&](Step<D> &st) {
+        if (p.rotate_k) {   // else the keys are stored rotated (ablation mode)
+            if (st.fast) {
+                // R(base + lc) = R(base) R(lc): the base row goes through the
+                // wave's LDS slot, R(lc) comes from the shared table
+                if (lane < HALF)
+                    *reinterpret_cast<f32x2 *>(reinterpret_cast<float *>(&s_row[wave][0][0]) +
+                                               ((lane / (HALF / 2)) & 1) * HALF + 2 * (lane % (HALF / 2))) = st.row;
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
                 for (int c = 0; c < NC / 2; ++c) {
-                    f32x4 c0, s0, c1, s1;
-                    rot(32 * c + 8 * lg, c0, s0);
-                    rot(32 * c + 8 * lg + 4, c1, s1);
-                    rope4<0>(cur.k[T][c], cur.k[T][c + NC / 2], c0, s0);
-                    rope4<1>(cur.k[T][c], cur.k[T][c + NC / 2], c1, s1);
+                    const int q0 = 8 * c + 2 * lg;
+                    const f32x4 cb0 = s_row[wave][0][q0], sb0 = s_row[wave][1][q0];
+                    const f32x4 cb1 = s_row[wave][0][q0 + 1], sb1 = s_row[wave][1][q0 + 1];
+                    const f32x4 co0 = s_dc[q0][lc], so0 = s_ds[q0][lc];
+                    const f32x4 co1 = s_dc[q0 + 1][lc], so1 = s_ds[q0 + 1][lc];
+                    rope4<0>(st.k[c], st.k[c + NC / 2], cb0 * co0 - sb0 * so0, sb0 * co0 + cb0 * so0);
+                    rope4<1>(st.k[c], st.k[c + NC / 2], cb1 * co1 - sb1 * so1, sb1 * co1 + cb1 * so1);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+            } else {
+                // positions that do not follow the block offsets: each key's own row
+                const int row = st.kpi >= 0 ? st.kpi : 0;
+                const f32x4 *cr = reinterpret_cast<const f32x4 *>(p.cos_tab + (size_t)row * HALF);
+                const f32x4 *sr = reinterpret_cast<const f32x4 *>(p.sin_tab + (size_t)row * HALF);
+#pragma unroll
+                for (int c = 0; c < NC / 2; ++c) {
+                    const int q0 = 8 * c + 2 * lg;
+                    rope4<0>(st.k[c], st.k[c + NC / 2], cr[q0], sr[q0]);
+                    rope4<1>(st.k[c], st.k[c + NC / 2], cr[q0 + 1], sr[q0 + 1]);
                 }
             }
-#pragma unroll
-            for (int c = 0; c < NC; ++c) sacc[T] = mfma16(cur.k[T][c], qop[c], sacc[T]);
         }
-        float sv[8];
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sacc = mfma16(st.k[c], qop[c], sacc);
+        // lane holds keys 4lg .. 4lg+3 of column lc
+        float sv[4];
         float mx = -INFINITY;
         bool any_bad = false;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int kp = cur.spi[e];
+        for (int e = 0; e < 4; ++e) {
+            const int kp = st.spi[e];
             const bool vis = kp >= 0 && kp <= pos;
             any_bad |= kp < 0;
-            sv[e] = vis ? sacc[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
+            sv[e] = vis ? sacc[e] * p.scale_log2 : -INFINITY;
             mx = fmaxf(mx, sv[e]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
-        float ls = 0.f;
+        if (__any(mx > m_ref + kSlack)) {
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = fast_exp2(m_ref - m_new);
+            m_ref = m_new;
+            l_run *= alpha;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sv[e] = fast_exp2(sv[e] - m_use);
-            ls += sv[e];
+            for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
         }
-        l_run = l_run * alpha + ls;
-        u32x4 pb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pb[e] = pack2(sv[2 * e], sv[2 * e + 1]);
-        // any unusable key in the step: zero its V channel entries so that
+        for (int e = 0; e < 4; ++e) {
+            sv[e] = fast_exp2(sv[e] - m_ref);
+            l_run += sv[e];
+        }
+        const u32x2 pb = {pack2(sv[0], sv[1]), pack2(sv[2], sv[3])};
+        // any unusable key in the step: zero its V entries so that
         // 0 * garbage cannot poison O
         if (__any(any_bad)) {
+            const uint32_t m0 = (st.spi[0] < 0 ? 0u : 0xffffu) | (st.spi[1] < 0 ? 0u : 0xffff0000u);
+            const uint32_t m1 = (st.spi[2] < 0 ? 0u : 0xffffu) | (st.spi[3] < 0 ? 0u : 0xffff0000u);
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint32_t w = cur.v[dt][e];
-                    if (cur.spi[2 * e] < 0) w &= 0xffff0000u;
-                    if (cur.spi[2 * e + 1] < 0) w &= 0x0000ffffu;
-                    cur.v[dt][e] = w;
-                }
+            for (int dt = 0; dt < D / 16; ++dt) {
+                st.v[dt][0] &= m0;
+                st.v[dt][1] &= m1;
+            }
         }
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma16(cur.v[dt], pb, acc[dt] * alpha);
+        for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma_k16(st.v[dt], pb, acc[dt]);
     };
-    // two step buffers in turn; the step after the range is requested too
-    // (clamped indices, zero page) so that no branch guards the requests
-    Step<D> sa, sb;
-    if (nsteps > 0) step_load<D>(p, sa, bt, pis, g, wbeg, key_end, lc, lg);
-    for (int it = 0; it < nsteps; it += 2) {
-        step_load<D>(p, sb, bt, pis, g, wbeg + 32 * (it + 1), key_end, lc, lg);
-        process(sa);
-        if (it + 1 >= nsteps) break;
-        step_load<D>(p, sa, bt, pis, g, wbeg + 32 * (it + 2), key_end, lc, lg);
-        process(sb);
+
+    // Positions run two steps ahead of K/V so that a step's rotation path and
+    // base row are known when its K/V are requested; everything a step needs
+    // is then requested before the previous step's math.  The steps after the
+    // range are requested too (clamped, all keys unusable), so no branch
+    // guards the requests.
+    const int nsteps = __builtin_amdgcn_readfirstlane(key_end > wbeg ? (key_end - wbeg + 15) / 16 : 0);
+    if (nsteps > 0) {
+        const int wb = __builtin_amdgcn_readfirstlane(wbeg);
+        const int lastb = __builtin_amdgcn_readfirstlane((key_end - 1) & ~15);
+        Pos pe, po;
+        Step<D> sa, sb;
+        pos_load(pe, bt, pis, wb, lastb, lc, lg);
+        pos_load(po, bt, pis, wb + 16, lastb, lc, lg);
+        step_issue<D>(p, sa, pe, g, wb, key_end, lane, lc, lg);
+        for (int it = 0; it < nsteps; it += 2) {
+            pos_load(pe, bt, pis, wb + 16 * (it + 2), lastb, lc, lg);
+            step_issue<D>(p, sb, po, g, wb + 16 * (it + 1), key_end, lane, lc, lg);
+            process(sa);
+            if (it + 1 >= nsteps) break;
+            pos_load(po, bt, pis, wb + 16 * (it + 3), lastb, lc, lg);
+            step_issue<D>(p, sa, pe, g, wb + 16 * (it + 2), key_end, lane, lc, lg);
+            process(sb);
+        }
     }
 
     // ---- merge the 4 waves of the workgroup through LDS
@@ -273,7 +327,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int i = 0; i < 4; ++i) s_o[wave][16 * dt + 4 * lg + i][lc] = acc[dt][i];
     if (lg == 0) {
-        s_m[wave][lc] = m_run;
+        s_m[wave][lc] = lt > 0.f ? m_ref : -INFINITY;
         s_l[wave][lc] = lt;
     }
     __syncthreads();
