@@ -177,6 +177,45 @@ def test_decode_matches_prefill_with_one_query():
     assert np.max(np.abs(l1.cpu().numpy() - l2.cpu().numpy())) <= 2e-3
 
 
+def _irregular_decode():
+    """Blocks whose usable keys do not sit at pi = base + offset (the decode
+    kernel then rotates each key with its own table row), next to regular
+    ones: positions shuffled inside every other block of request 0, a block
+    whose base would be negative in request 1, and a hole inside a block of
+    request 2 that the following slots do not skip."""
+    w = W.decode_heavy(batch=3, n_spans=2, span_tok=300, private_spans=True, Hq=32)
+    rng = np.random.default_rng(11)
+    kp = w.kv_pos
+    for b in range(0, int(w.kv_len[0]) // 16, 2):
+        kp[0, 16 * b:16 * b + 16] = rng.permutation(kp[0, 16 * b:16 * b + 16])
+    kp[1, 0:16] = np.concatenate([[-1, -1, -1], np.arange(13)])
+    kp[2, 40] = -1
+    kp[2, 41:48] -= 1
+    return w
+
+
+@pytest.mark.parametrize("name", ["irregular_blocks", "fused_long_context_small", "fused_shared_small"])
+def test_decode_irregular_positions(name):
+    if name == "irregular_blocks":
+        w = _irregular_decode()
+    else:
+        # fresh rows sit in appended private blocks at the stale slots' scattered positions
+        src = small_select_workloads()[name[len("fused_"):]]()
+        ref_off, ref_idx = oracle.select(src, oracle.mass(src))
+        req_off = H.req_offsets(src, ref_off)
+        n = int(req_off[-1])
+        pk, pv, kp, kl = oracle.fuse(src, ref_idx, req_off, src.fresh_k[:n], src.fresh_v[:n])
+        fused = src.copy()
+        fused.pool_k, fused.pool_v, fused.kv_pos, fused.kv_len = pk, pv, kp, kl
+        w = _last_token_decode(fused)
+    say(f"decode {name}: B={w.batch} kv={w.kv_len.tolist()[:6]}")
+    ctx = H.ctx_for(w)
+    out, lse, _ = H.decode(ctx, w)
+    ref_o, ref_l = oracle.attention(w)
+    compare_out(H.host_bf16(out), ref_o, "O")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+
+
 # ------------------------------------------------------------- selection
 
 def small_select_workloads():
