@@ -172,13 +172,26 @@ __device__ __forceinline__ void vmap(int tid, int &half, int &dd) {
     dd = (l & 7) | ((l >> 4) << 3);
 }
 
+// Staging geometry: staging task u of a thread covers key
+// kk = tid / PC + u * (NT / PC) of the 64-key tile, channels 8pc..8pc+7 of
+// each half of d (pc = tid % PC).  One wave's keys of one task are 64 / PC
+// consecutive keys (8 or 16) starting at a multiple of 64 / PC, so they lie in
+// one pool block: the block id is wave-uniform (a scalar load) and a lane's
+// row inside the block never changes from tile to tile.
+template <int D, int WAVES>
+__device__ __forceinline__ int task_key0(int wave, int u) {   // first key of (wave, task u)
+    using GG = Geo<D, WAVES>;
+    return wave * (64 / GG::PC) + u * (GG::NT / GG::PC);
+}
+
 // Block ids / positions of one tile for this thread's staging tasks, as
 // loaded (at clamped indices); the range check is applied where they are used,
 // one tile later, so that no wait for these loads sits at the tile start.
 template <int D, int WAVES>
 struct Meta {
-    int32_t kblk[Geo<D, WAVES>::KTASK], kpi[Geo<D, WAVES>::KTASK];
-    int32_t vblk;
+    int32_t kblk[Geo<D, WAVES>::KTASK];   // wave-uniform
+    int32_t kpi[Geo<D, WAVES>::KTASK];
+    int32_t vblk;      // wave-uniform
     int32_t vkey_pi;   // lanes 0..15: pi of key lane of this wave's V block
 };
 
@@ -193,58 +206,65 @@ struct Data {
 };
 
 // Unconditional loads at clamped indices, then select: no divergent branches.
-// kv_stride (a multiple of 16) bounds every index: a V chunk's 8 positions
-// start at a multiple of 8 below key_end <= kv_stride, so they never cross it.
+// Blocks past the range clamp to the block of the last key; kv_stride (a
+// multiple of 16) bounds every position index, since a clamped block index
+// times 16 plus a row below 16 stays below it.
 template <int D, int WAVES>
 __device__ __forceinline__ void meta_load(Meta<D, WAVES> &m, const int32_t *bt, const int32_t *pis, int tile,
                                           int key_end, int tid) {
     using GG = Geo<D, WAVES>;
-    const int last = key_end - 1;   // key_end >= 1; tiles past the range clamp to the last key
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int lastb = (key_end - 1) >> 4;   // key_end >= 1
 #pragma unroll
     for (int u = 0; u < GG::KTASK; ++u) {
-        const int jc = min(tile + tid / GG::PC + u * (GG::NT / GG::PC), last);
-        m.kblk[u] = bt[jc >> 4];
-        m.kpi[u] = pis[jc];
+        const int kb = tile + task_key0<D, WAVES>(wave, u);
+        const int bc = min(kb >> 4, lastb);
+        m.kblk[u] = bt[bc];
+        m.kpi[u] = pis[(uint32_t)(bc * 16 + (kb & 15) + lane / GG::PC)];
     }
     // V staging: every lane of this wave covers keys of tile block (wave & 3)
-    const int jb = tile + 16 * ((tid >> 6) & 3);
-    m.vblk = bt[min(jb, last) >> 4];
-    m.vkey_pi = pis[min(jb + (tid & 15), last)];
+    const int bv = min((tile >> 4) + (wave & 3), lastb);
+    m.vblk = bt[bv];
+    m.vkey_pi = pis[(uint32_t)(bv * 16 + (lane & 15))];
 }
 
 template <int D, int WAVES>
 __device__ __forceinline__ void data_load(const FwdParams &p, Data<D, WAVES> &dt, const Meta<D, WAVES> &m, int g,
                                           int tile, int key_end, int tid, bool need_v) {
     using GG = Geo<D, WAVES>;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int pc = lane % GG::PC;
 #pragma unroll
     for (int u = 0; u < GG::KTASK; ++u) {
-        const int kk = tid / GG::PC + u * (GG::NT / GG::PC);
-        const int pc = tid % GG::PC;
-        const int j = tile + kk;
-        const int blk = m.kblk[u], pi = m.kpi[u];
-        const bool ok = j < key_end && (unsigned)blk < (unsigned)p.num_blocks && (unsigned)pi < (unsigned)p.max_pos;
+        const int kb = tile + task_key0<D, WAVES>(wave, u);
+        const int row = (kb & 15) + lane / GG::PC;   // row inside the block
+        const int blk = __builtin_amdgcn_readfirstlane(m.kblk[u]), pi = m.kpi[u];
+        const bool bok = (unsigned)blk < (unsigned)p.num_blocks;
+        const bool ok = bok && (kb & ~15) + row < key_end && (unsigned)pi < (unsigned)p.max_pos;
         dt.kpi[u] = ok ? pi : -1;
-        // unusable keys read the zero page: no branch, and they rotate to zero
-        const uint16_t *row = ok ? p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + (j & 15)) * D : p.zero_page;
-        dt.klo[u] = *reinterpret_cast<const u32x4 *>(row + 8 * pc);
-        dt.khi[u] = *reinterpret_cast<const u32x4 *>(row + GG::HALF + 8 * pc);
+        // an unusable block reads the zero page; unusable keys of a usable
+        // block are masked (scores) and zeroed (V) downstream
+        const uint16_t *kbase = bok ? p.k_pool + ((size_t)blk * p.hkv + g) * (kBlock * D) : p.zero_page;
+        const uint32_t off = (uint32_t)(row * D + 8 * pc);
+        dt.klo[u] = *reinterpret_cast<const u32x4 *>(kbase + off);
+        dt.khi[u] = *reinterpret_cast<const u32x4 *>(kbase + off + GG::HALF);
     }
     if (!need_v) return;
     int half, dd;
     vmap(tid, half, dd);
-    const int jb = tile + 16 * ((tid >> 6) & 3);
-    const bool bok = jb < key_end && (unsigned)m.vblk < (unsigned)p.num_blocks;
+    const int jb = tile + 16 * (wave & 3);
+    const int vblk = __builtin_amdgcn_readfirstlane(m.vblk);
+    const bool bok = jb < key_end && (unsigned)vblk < (unsigned)p.num_blocks;
     // validity of the block's 16 keys: lanes 0..15 hold their pi; the ballot
     // lands in scalar registers
-    const bool kv_ok = jb + (tid & 15) < key_end && (unsigned)m.vkey_pi < (unsigned)p.max_pos;
+    const bool kv_ok = jb + (lane & 15) < key_end && (unsigned)m.vkey_pi < (unsigned)p.max_pos;
     const uint32_t okmask = (uint32_t)__ballot(kv_ok) & 0xffffu;
     dt.vmask = bok ? (int32_t)((~okmask >> (8 * half)) & 0xffu) : 0xff;
-    const int32_t vm = dt.vmask;
-    const uint16_t *vb = bok ? p.v_pool + ((size_t)m.vblk * p.hkv + g) * D * kBlock + 8 * half : p.zero_page;
+    const uint16_t *vb = bok ? p.v_pool + ((size_t)vblk * p.hkv + g) * (D * kBlock) : p.zero_page;
 #pragma unroll
     for (int u = 0; u < GG::VCH; ++u) {
         const int d = dd + 32 * ((tid >> 8) + u * (GG::NT / 256));
-        dt.v[u] = *reinterpret_cast<const u32x4 *>(vb + (size_t)d * kBlock);
+        dt.v[u] = *reinterpret_cast<const u32x4 *>(vb + (uint32_t)(d * kBlock + 8 * half));
     }
 }
 
@@ -257,13 +277,35 @@ __device__ __forceinline__ void cs_load(const FwdParams &p, Data<D, WAVES> &dt, 
     for (int u = 0; u < GG::KTASK; ++u) {
         const int pc = tid % GG::PC;
         const int pi = dt.kpi[u];
-        const float *cr = p.cos_tab + (size_t)(pi >= 0 ? pi : 0) * GG::HALF + 8 * pc;
-        const float *sr = p.sin_tab + (size_t)(pi >= 0 ? pi : 0) * GG::HALF + 8 * pc;
-        dt.cs[u][0] = *reinterpret_cast<const f32x4 *>(cr);
-        dt.cs[u][1] = *reinterpret_cast<const f32x4 *>(cr + 4);
-        dt.cs[u][2] = *reinterpret_cast<const f32x4 *>(sr);
-        dt.cs[u][3] = *reinterpret_cast<const f32x4 *>(sr + 4);
+        const uint32_t off = (uint32_t)((pi >= 0 ? pi : 0) * GG::HALF + 8 * pc);
+        dt.cs[u][0] = *reinterpret_cast<const f32x4 *>(p.cos_tab + off);
+        dt.cs[u][1] = *reinterpret_cast<const f32x4 *>(p.cos_tab + off + 4);
+        dt.cs[u][2] = *reinterpret_cast<const f32x4 *>(p.sin_tab + off);
+        dt.cs[u][3] = *reinterpret_cast<const f32x4 *>(p.sin_tab + off + 4);
     }
+}
+
+// First key of [key_begin, key_end) that is unusable or not visible to the
+// row with the smallest position (INT_MAX if none).  Four keys per thread and
+// step with no early exit, so the loads of all steps can be in flight at once.
+// key_begin is a multiple of 64 and kv_stride of 16, so each 4-key load is
+// aligned and stays inside the request's position row.
+template <int NT>
+__device__ __forceinline__ int first_bad_key(const FwdParams &p, const int32_t *bt, const int32_t *pis, int key_begin,
+                                             int key_end, int min_pos, int tid) {
+    int bad = 0x7fffffff;
+#pragma unroll 4
+    for (int j0 = key_begin + 4 * tid; j0 < key_end; j0 += 4 * NT) {
+        const i32x4 pi = *reinterpret_cast<const i32x4 *>(pis + j0);
+        const int blk = bt[j0 >> 4];
+        const bool bok = blk >= 0 && blk < p.num_blocks;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool good = bok && pi[i] >= 0 && pi[i] < p.max_pos && pi[i] <= min_pos;
+            if (j0 + i < key_end && !good) bad = min(bad, j0 + i);
+        }
+    }
+    return bad;
 }
 
 // Rotate and write one tile into an LDS buffer.  Returns whether every key
@@ -440,12 +482,9 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     // First key of this workgroup's range that is unusable or not visible to
     // every row (pi and block ids are small and L2-resident): tiles before it
     // need no mask.
-    for (int j = key_begin + tid; j < key_end; j += GG::NT) {
-        const int pi = pis[j], blk = bt[j >> 4];
-        if (!(pi >= 0 && pi < p.max_pos && pi <= min_pos && blk >= 0 && blk < p.num_blocks)) {
-            atomicMin(&s_firstbad, j);
-            break;
-        }
+    {
+        const int bad = first_bad_key<GG::NT>(p, bt, pis, key_begin, key_end, min_pos, tid);
+        if (bad != 0x7fffffff) atomicMin(&s_firstbad, bad);
     }
     __syncthreads();
     const int first_bad = s_firstbad;
@@ -862,12 +901,9 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
     }
     __syncthreads();
     const int min_pos = s_minpos;
-    for (int j = key_begin + tid; j < key_end; j += GG::NT) {
-        const int pi = pis[j], blk = bt[j >> 4];
-        if (!(pi >= 0 && pi < p.max_pos && pi <= min_pos && blk >= 0 && blk < p.num_blocks)) {
-            atomicMin(&s_firstbad, j);
-            break;
-        }
+    {
+        const int bad = first_bad_key<GG::NT>(p, bt, pis, key_begin, key_end, min_pos, tid);
+        if (bad != 0x7fffffff) atomicMin(&s_firstbad, bad);
     }
     __syncthreads();
     const int first_bad = s_firstbad;
