@@ -111,16 +111,22 @@ def calibrate_copy():
 
 def _pmc(d, counter, name_part, every=1):
     """Mean counter value over the dispatches of kernels named like name_part
-    (every: take every n-th of them in dispatch order, from the first)."""
+    (every: take every n-th of them in dispatch order, from the first).  With
+    every > 1 the dispatches must all have one grid size and come in whole
+    groups of `every`, else the run held other launches of the kernel."""
     rows = []
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
-                rows.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
-    rows = sorted(rows)[::every]
+                rows.append((int(r["Dispatch_Id"]), float(r["Counter_Value"]), r.get("Grid_Size", "")))
+    rows = sorted(rows)
+    if every > 1 and (len({g for _, _, g in rows}) > 1 or len(rows) % every):
+        raise SystemExit(f"{d}: {len(rows)} dispatches of '{name_part}' with grids {sorted({g for _, _, g in rows})}; "
+                         "profile the step alone (--no-decode --no-recompute --no-anchor --no-ablation --no-hashing)")
+    rows = rows[::every]
     if not rows:
         raise SystemExit(f"no {counter} rows for '{name_part}' under {d}")
-    return float(np.mean([v for _, v in rows])), len(rows)
+    return float(np.mean([v for _, v, _ in rows])), len(rows)
 
 
 def traffic_from(copy_fetch, copy_write, fetch, write):
