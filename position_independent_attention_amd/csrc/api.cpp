@@ -17,6 +17,7 @@ struct pic_ctx {
     pic_config cfg{};
     float *cos_d = nullptr;
     float *sin_d = nullptr;
+    double *rev_d = nullptr;      // [d/2] theta^(-2i/d) / (2 pi): revolutions per position
     uint16_t *zero_d = nullptr;   // zero page read in place of unusable keys
     std::string err;
 };
@@ -75,7 +76,8 @@ FwdPlan plan_fwd(const pic_config &c, int batch, int max_q_len, int max_kv_len) 
     return pl;
 }
 
-// Decode: about four 256-thread workgroups per CU in total, each covering
+// Decode: about four 256-thread workgroups per CU in total (or one resident
+// round when that would leave a second round mostly idle), each covering
 // split_len keys (a multiple of 4 waves x 32 keys, at least 512) of one
 // (request, kv head).
 struct DecodePlan {
@@ -90,6 +92,16 @@ DecodePlan plan_decode(int batch, int hkv, int max_kv_len) {
     const long long per = (rows * max_kv_len + 4LL * kCUs - 1) / (4LL * kCUs);
     long long len = (per + 127) / 128 * 128;
     len = std::max(512LL, std::min(len, ((long long)max_kv_len + 127) / 128 * 128));
+    // Two workgroups per CU are resident at once.  A plan that overflows one
+    // such round by less than a whole round would leave its second round
+    // mostly idle: take one round of longer splits instead.
+    const long long resident = 2LL * kCUs;
+    const long long nwg = rows * ((max_kv_len + len - 1) / len);
+    if (nwg > resident && nwg < 2 * resident) {
+        const long long per_row = std::max(1LL, resident / rows);
+        len = ((max_kv_len + per_row - 1) / per_row + 127) / 128 * 128;
+        len = std::max(512LL, len);
+    }
     d.split_len = (int)len;
     d.num_splits = (int)((max_kv_len + len - 1) / len);
     return d;
@@ -250,10 +262,14 @@ pic_status pic_ctx_create(const pic_config *cfg, pic_ctx **out) {
             cs[(size_t)p * half + i] = (float)std::cos(a);
             sn[(size_t)p * half + i] = (float)std::sin(a);
         }
+    std::vector<double> rev(half);
+    for (int i = 0; i < half; ++i) rev[i] = inv[i] / (2.0 * 3.14159265358979323846);
     hipError_t e = hipMalloc(&ctx->cos_d, n * sizeof(float));
     if (e == hipSuccess) e = hipMalloc(&ctx->sin_d, n * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc(&ctx->rev_d, half * sizeof(double));
     if (e == hipSuccess) e = hipMemcpy(ctx->cos_d, cs.data(), n * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(ctx->sin_d, sn.data(), n * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(ctx->rev_d, rev.data(), half * sizeof(double), hipMemcpyHostToDevice);
     const size_t zbytes = (size_t)cfg->head_dim * PIC_BLOCK_SIZE * sizeof(uint16_t);
     if (e == hipSuccess) e = hipMalloc(&ctx->zero_d, zbytes);
     if (e == hipSuccess) e = hipMemset(ctx->zero_d, 0, zbytes);
@@ -269,6 +285,7 @@ void pic_ctx_destroy(pic_ctx *ctx) {
     if (!ctx) return;
     if (ctx->cos_d) (void)hipFree(ctx->cos_d);
     if (ctx->sin_d) (void)hipFree(ctx->sin_d);
+    if (ctx->rev_d) (void)hipFree(ctx->rev_d);
     if (ctx->zero_d) (void)hipFree(ctx->zero_d);
     delete ctx;
 }
@@ -389,6 +406,7 @@ pic_status pic_attn_decode(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
     p.group = c.num_q_heads / c.num_kv_heads;
     p.cos_tab = ctx->cos_d;
     p.sin_tab = ctx->sin_d;
+    p.rev_freq = ctx->rev_d;
     p.rotate_k = c.keys_prerotated ? 0 : 1;
     p.max_pos = c.max_position;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));

@@ -16,12 +16,13 @@
 // pi = base + offset (the usual case, also for a span reused at another
 // offset), R(pi) = R(base) R(offset); the block's base cos/sin row (512 bytes
 // at d = 128) is requested with the block and passed through LDS, and R(o)
-// for o = 0..15 sits in LDS for the whole kernel.  Any other block reads each
-// key's own table row.  Positions are requested two blocks ahead, so a
-// block's path and base row are known when its keys are requested, and every
-// load of a block is issued before the previous block's math (memory
-// requests retire in order, so a load issued later would also wait for the
-// prefetch).
+// for o = 0..15 sits in LDS for the whole kernel.  Any other block computes
+// each key's cos/sin from its angle (fp64 reduction to one revolution, then
+// the hardware sin/cos), so that it needs no memory request at all.
+// Positions are requested two blocks ahead, so a block's path and base row
+// are known when its keys are requested, and every load of a block is issued
+// before the previous block's math (memory requests retire in order, so a
+// load issued later would also wait for the prefetch).
 //
 // A workgroup (4 waves) covers split_len keys of one (request, kv head);
 // waves are merged through LDS and splits by the LSE merge kernel.
@@ -148,6 +149,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __shared__ f32x4 s_dc[NQ][16], s_ds[NQ][16];
     // each wave's current block-base row: cos, then sin
     __shared__ f32x4 s_row[kWaves][2][NQ];
+    // revolutions per position of each frequency, theta^(-2i/d) / (2 pi)
+    __shared__ double s_rf[HALF];
     __shared__ float s_o[kWaves][D][16];
     __shared__ float s_m[kWaves][16], s_l[kWaves][16];
 
@@ -161,6 +164,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lc = lane & 15, lg = lane >> 4;
+    for (int t = tid; t < HALF; t += kThreads) s_rf[t] = p.rev_freq[t];
     for (int t = tid; t < NQ * 16; t += kThreads) {
         const int o = t & 15, q4 = t >> 4;
         const bool in = o < p.max_pos;
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     f32x4 acc[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    __syncthreads();   // R(o) table
+    __syncthreads();   // R(o) and revolution tables
 
     auto process = [&](Step<D> &st) {
         if (p.rotate_k) {   // else the keys are stored rotated (ablation mode)
@@ -235,15 +239,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
             } else {
-                // positions that do not follow the block offsets: each key's own row
-                const int row = st.kpi >= 0 ? st.kpi : 0;
-                const f32x4 *cr = reinterpret_cast<const f32x4 *>(p.cos_tab + (size_t)row * HALF);
-                const f32x4 *sr = reinterpret_cast<const f32x4 *>(p.sin_tab + (size_t)row * HALF);
+                // positions that do not follow the block offsets: cos/sin of
+                // each key's own angle, computed here rather than read from
+                // the table (a table read issued now would also wait for the
+                // next step's requests): pi * theta_i / (2 pi) in fp64, its
+                // fractional part, then the hardware sin/cos of a fraction of
+                // a revolution
+                const double pd = (double)(st.kpi >= 0 ? st.kpi : 0);
+                auto angle_cs = [&](int f0, f32x4 &cc, f32x4 &ss) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        double rv = pd * s_rf[f0 + e];
+                        rv -= __builtin_rint(rv);
+                        const float r = (float)rv;
+                        cc[e] = __builtin_amdgcn_cosf(r);
+                        ss[e] = __builtin_amdgcn_sinf(r);
+                    }
+                };
 #pragma unroll
                 for (int c = 0; c < NC / 2; ++c) {
-                    const int q0 = 8 * c + 2 * lg;
-                    rope4<0>(st.k[c], st.k[c + NC / 2], cr[q0], sr[q0]);
-                    rope4<1>(st.k[c], st.k[c + NC / 2], cr[q0 + 1], sr[q0 + 1]);
+                    f32x4 c0, s0, c1, s1;
+                    angle_cs(32 * c + 8 * lg, c0, s0);
+                    angle_cs(32 * c + 8 * lg + 4, c1, s1);
+                    rope4<0>(st.k[c], st.k[c + NC / 2], c0, s0);
+                    rope4<1>(st.k[c], st.k[c + NC / 2], c1, s1);
                 }
             }
         }

@@ -65,6 +65,7 @@ struct DecodeParams {
     int32_t hq, hkv, group;
     const float *cos_tab;
     const float *sin_tab;
+    const double *rev_freq;   // [d/2] theta^(-2i/d) / (2 pi): revolutions per position
     int32_t rotate_k;         // 0: keys are stored rotated (ablation mode)
     int32_t max_pos;
     float scale_log2;
