@@ -31,10 +31,21 @@ __global__ __launch_bounds__(256) void mass_reduce_kernel(SelectParams p) {
     if (j >= kvl) return;
     const int nrows = (p.q_start[r + 1] - p.q_start[r]) * p.group;
     const int nrb = min(p.row_blocks, (nrows + p.rows_per_block - 1) / p.rows_per_block);
+    // partials in (kv head, row block) order, summed in that order; the loads
+    // of a group of 16 are all in flight before the first add
+    const int n = p.hkv * nrb;
+    const float *mp = p.mass_part + (size_t)r * p.hkv * p.row_blocks * p.mass_stride + j;
+    auto at = [&](int i) { return mp[((size_t)(i / nrb) * p.row_blocks + i % nrb) * p.mass_stride]; };
     float s = 0.f;
-    for (int g = 0; g < p.hkv; ++g)
-        for (int rb = 0; rb < nrb; ++rb)
-            s += p.mass_part[(((size_t)r * p.hkv + g) * p.row_blocks + rb) * p.mass_stride + j];
+    int i = 0;
+    for (; i + 16 <= n; i += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = at(i + u);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s += v[u];
+    }
+    for (; i < n; ++i) s += at(i);
     p.mass[(size_t)r * p.kv_stride + j] = s;
 }
 
