@@ -13,6 +13,11 @@ d = 128, theta 5e5):
 (plus two small device copies that restore the un-fused pi / kv_len so that
 every step starts from the same cache).
 
+The step is captured once as a HIP graph and replayed once per timed step
+(each replay first checked bit for bit against an eager step); --no-graph
+times it eagerly.  Per-op times come from an eager run with events between
+the calls.
+
 metric: attended KV tokens per second, where each attention-type call over a
 request attends its kv_len minus masked slots (33,024 here) and the step makes
 four such calls.  The roofline object is for the dominant kernel (step 1,
@@ -167,6 +172,7 @@ def main():
     ap.add_argument("--no-anchor", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--no-hashing", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time the step eagerly, without a HIP graph")
     ap.add_argument("--decode-private", action="store_true",
                     help="decode line on the unshared control (4 GiB pool)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -230,22 +236,23 @@ def main():
     stream = torch.cuda.current_stream()
     names = ["prefill", "select", "fuse", "prefill_fused", "decode"]
 
-    def step(evs=None):
+    def step(evs=None, st=None):
+        st = stream if st is None else st
         dc.kv_pos.copy_(kv_pos0)
         dc.kv_len.copy_(kv_len0)
         dc.max_kv_len = kv0
-        if evs: evs[0].record(stream)
-        pic.pic_attn_prefill(ctx, dc, out1, lse1, ws=ws, stream=stream)
-        if evs: evs[1].record(stream)
-        pic.qc_score_select(ctx, dc, lse1, nsel, sel, None, ws=ws, stream=stream)
-        if evs: evs[2].record(stream)
-        pic.kv_fuse_scatter(ctx, dc, sel, req_off, fk, fv, nsel, nsel, stream=stream)
-        if evs: evs[3].record(stream)
+        if evs: evs[0].record(st)
+        pic.pic_attn_prefill(ctx, dc, out1, lse1, ws=ws, stream=st)
+        if evs: evs[1].record(st)
+        pic.qc_score_select(ctx, dc, lse1, nsel, sel, None, ws=ws, stream=st)
+        if evs: evs[2].record(st)
+        pic.kv_fuse_scatter(ctx, dc, sel, req_off, fk, fv, nsel, nsel, stream=st)
+        if evs: evs[3].record(st)
         dc.max_kv_len = kv_fused
-        pic.pic_attn_prefill(ctx, dc, out2, None, ws=ws, stream=stream)
-        if evs: evs[4].record(stream)
-        pic.pic_attn_decode(ctx, dcd, q_dec, qpos_dec, out3, None, ws=ws, stream=stream)
-        if evs: evs[5].record(stream)
+        pic.pic_attn_prefill(ctx, dc, out2, None, ws=ws, stream=st)
+        if evs: evs[4].record(st)
+        pic.pic_attn_decode(ctx, dcd, q_dec, qpos_dec, out3, None, ws=ws, stream=st)
+        if evs: evs[5].record(st)
 
     for _ in range(args.warmup):
         step()
@@ -258,10 +265,48 @@ def main():
         step(evs[k])
     stop.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(stop) / args.steps
+    ms_eager = start.elapsed_time(stop) / args.steps
     op_ms = {n: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
              for i, n in enumerate(names)}
     log("per-op ms:", {k: round(v, 4) for k, v in op_ms.items()})
+
+    # The same step captured once as a HIP graph and replayed K times: the step
+    # makes 14 launches, and a replay drops their host-side launch work and most
+    # of the gaps between them.  Every replay is first checked bit for bit
+    # against an eager step (with eager work and synchronisations in between).
+    ms_graph, graph_note = None, "off"
+    if not args.no_graph:
+        outs = (out1, lse1, sel, out2, out3)
+        step()
+        torch.cuda.synchronize()
+        ref = [o.clone() for o in outs]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(st=torch.cuda.current_stream())
+        same = True
+        for _ in range(3):
+            for o in outs:
+                o.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            same = same and all(torch.equal(o, r) for o, r in zip(outs, ref))
+        if same:
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            start.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            stop.record(stream)
+            torch.cuda.synchronize()
+            ms_graph = start.elapsed_time(stop) / args.steps
+            graph_note = "hip graph, one replay per step (replays checked bitwise against an eager step)"
+        else:
+            graph_note = "graph replay differed from the eager step: eager timing reported"
+            log(graph_note)
+        del g
+    ms_per_step = ms_graph if ms_graph is not None else ms_eager
 
     tokens = attended_tokens(w)
     step_tokens = 4 * tokens
@@ -277,6 +322,7 @@ def main():
 
     result = {"metric": METRIC, "value": round(value, 1), "unit": "attended KV tokens/s", "n_gpus": 1,
               "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+              "ms_per_step_eager": round(ms_eager, 5), "launch": graph_note,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
               "data": "synthetic",
               "config": {"workload": "long_context_qc_fusion", "batch": 1, "kv_slots": int(w.max_kv_len),
