@@ -47,7 +47,7 @@ pic_status hip_fail(pic_ctx *ctx, hipError_t e, const char *where) {
 
 // Launch geometry of the prefill-style kernels.
 struct FwdPlan {
-    int shape = 0;        // kernel variant, see pic::fwd_rows_per_block
+    int shape = 0;        // kernel variant (0, 1, 2: 1 with tile skipping), see pic::launch_fwd
     int rows_per_block = 64;
     int row_blocks = 0;
     int split_len = pic::kTileN;
@@ -61,9 +61,12 @@ FwdPlan plan_fwd(const pic_config &c, int batch, int max_q_len, int max_kv_len) 
     pl.shape = rows >= 128 ? 1 : 0;
     pl.rows_per_block = pic::fwd_rows_per_block(c.head_dim, pl.shape);
     pl.row_blocks = (int)((rows + pl.rows_per_block - 1) / pl.rows_per_block);
+    // many row blocks hold queries at many different positions: take the
+    // variant that skips the tiles no row of a workgroup sees
+    if (pl.shape == 1 && pl.row_blocks >= 8) pl.shape = 2;
     const long long base = (long long)pl.row_blocks * c.num_kv_heads * batch;
     // the big shape runs one 512-thread workgroup per CU, the small one several
-    const long long target = pl.shape == 1 && c.head_dim == 128 ? kCUs : 2 * kCUs;
+    const long long target = pl.shape >= 1 && c.head_dim == 128 ? kCUs : 2 * kCUs;
     int splits = 1;
     if (base > 0 && max_kv_len > 0) {
         const long long want = (target + base - 1) / base;

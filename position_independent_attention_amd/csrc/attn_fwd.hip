@@ -52,6 +52,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kRescaleSlack = 8.0f;   // log2 units
+constexpr int kNeedWords = 256;         // tile bit mask of a workgroup: up to 8,192 tiles
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -289,20 +290,29 @@ __device__ __forceinline__ void cs_load(const FwdParams &p, Data<D, WAVES> &dt, 
 // row with the smallest position (INT_MAX if none).  Four keys per thread and
 // step with no early exit, so the loads of all steps can be in flight at once.
 // key_begin is a multiple of 64 and kv_stride of 16, so each 4-key load is
-// aligned and stays inside the request's position row.
+// aligned and stays inside the request's position row.  With s_need, also
+// sets bit t of s_need for every 64-key tile t holding a usable key that the
+// row with the largest position (max_row) sees.
 template <int NT>
 __device__ __forceinline__ int first_bad_key(const FwdParams &p, const int32_t *bt, const int32_t *pis, int key_begin,
-                                             int key_end, int min_pos, int tid) {
+                                             int key_end, int min_pos, int tid, int max_row = -1,
+                                             uint32_t *s_need = nullptr) {
     int bad = 0x7fffffff;
 #pragma unroll 4
     for (int j0 = key_begin + 4 * tid; j0 < key_end; j0 += 4 * NT) {
         const i32x4 pi = *reinterpret_cast<const i32x4 *>(pis + j0);
         const int blk = bt[j0 >> 4];
         const bool bok = blk >= 0 && blk < p.num_blocks;
+        bool need = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool good = bok && pi[i] >= 0 && pi[i] < p.max_pos && pi[i] <= min_pos;
-            if (j0 + i < key_end && !good) bad = min(bad, j0 + i);
+            const bool usable = j0 + i < key_end && bok && pi[i] >= 0 && pi[i] < p.max_pos;
+            if (j0 + i < key_end && !(usable && pi[i] <= min_pos)) bad = min(bad, j0 + i);
+            need = need || (usable && pi[i] <= max_row);
+        }
+        if (s_need && need) {
+            const int t = (j0 - key_begin) >> 6;   // the 4 keys share a tile
+            atomicOr(&s_need[t >> 5], 1u << (t & 31));
         }
     }
     return bad;
@@ -356,7 +366,9 @@ __device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uin
     return full;
 }
 
-template <int D, int QG, int WAVES, int MODE>
+// SKIP: skip the tiles whose keys no row of the workgroup sees (launched for
+// requests with many row blocks, whose positions differ from block to block).
+template <int D, int QG, int WAVES, int MODE, bool SKIP>
 __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     using GG = Geo<D, WAVES>;
     constexpr int BM = 16 * QG * WAVES;
@@ -365,7 +377,9 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t Vs[kV ? 2 * GG::VBUF : 8];
     __shared__ __attribute__((aligned(16))) int32_t s_pi[2 * kTileN];
     __shared__ float s_red[MODE == kMass ? 2 * WAVES * kTileN : 1];
-    __shared__ int32_t s_minpos, s_firstbad;
+    __shared__ int32_t s_minpos, s_firstbad, s_maxpos;
+    // bit t: tile t holds a key that some row of the workgroup sees
+    __shared__ uint32_t s_need[SKIP ? kNeedWords : 1];
 
     const int nwg = p.row_blocks * p.hkv * p.num_splits * p.batch;
     int lid = xcd_remap(blockIdx.x, nwg);
@@ -395,13 +409,16 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     if (tid == 0) {
         s_minpos = 0x7fffffff;
         s_firstbad = 0x7fffffff;
+        s_maxpos = -1;
     }
+    if constexpr (SKIP)
+        for (int w = tid; w < kNeedWords; w += GG::NT) s_need[w] = 0u;
 
     // ---- this lane's query columns: load, rotate at q_pos, keep as B operands
     u32x4 qop[QG][GG::NC];
     int qpos[QG], qt[QG], qh[QG];
     bool qvalid[QG];
-    int my_min = 0x7fffffff;
+    int my_min = 0x7fffffff, my_max = -1;
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
         const int row = rb * BM + wave * 16 * QG + 16 * qg + lc;
@@ -412,7 +429,10 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         int pos = qvalid[qg] ? p.q_pos[qt[qg]] : -1;
         if (pos >= p.max_pos) pos = -1;
         qpos[qg] = pos;
-        if (qvalid[qg]) my_min = min(my_min, pos);
+        if (qvalid[qg]) {
+            my_min = min(my_min, pos);
+            my_max = max(my_max, pos);
+        }
 #pragma unroll
         for (int c = 0; c < GG::NC; ++c) qop[qg][c] = u32x4{0, 0, 0, 0};
         if (pos >= 0) {
@@ -464,11 +484,13 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
 
     __syncthreads();
     atomicMin(&s_minpos, my_min);
+    if constexpr (SKIP) atomicMax(&s_maxpos, my_max);
     const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
     // Staging pipeline: the data of tile t+2 (and the block ids of t+3) are
     // requested next to the QK of tile t+1, about a tile before they are
     // rotated and stored; indices past the range are clamped and such keys
-    // read the zero page, so the requests need no branch.
+    // read the zero page, so the requests need no branch.  Tiles 0 and 1 are
+    // requested before it is known which tiles the rows need.
     Meta<D, WAVES> m1, m2;
     Data<D, WAVES> dnext;
     if (ntiles > 0) {
@@ -479,16 +501,51 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     }
     __syncthreads();
     const int min_pos = s_minpos;
+    // Tiles with no key that any row sees are skipped (not in mass mode, which
+    // writes every key's partial sum); so is every tile when too many for the
+    // bit mask.
+    const bool skip = SKIP && MODE != kMass && ntiles <= kNeedWords * 32;
     // First key of this workgroup's range that is unusable or not visible to
     // every row (pi and block ids are small and L2-resident): tiles before it
     // need no mask.
     {
-        const int bad = first_bad_key<GG::NT>(p, bt, pis, key_begin, key_end, min_pos, tid);
+        const int bad = SKIP ? first_bad_key<GG::NT>(p, bt, pis, key_begin, key_end, min_pos, tid, s_maxpos,
+                                                     skip ? s_need : nullptr)
+                             : first_bad_key<GG::NT>(p, bt, pis, key_begin, key_end, min_pos, tid);
         if (bad != 0x7fffffff) atomicMin(&s_firstbad, bad);
     }
     __syncthreads();
     const int first_bad = s_firstbad;
-    if (ntiles > 0) {
+    // Whether the rows need every tile (the usual case): then the tile order
+    // is plain, with no look-up in the mask.  Each wave checks the whole mask.
+    bool every = !skip;
+    if (SKIP && skip) {
+        bool miss = false;
+        for (int w = lane; w < kNeedWords; w += 64) {
+            const int lo = 32 * w, n = min(max(ntiles - lo, 0), 32);
+            const uint32_t want = n == 32 ? 0xffffffffu : ((1u << n) - 1u);
+            miss = miss || (s_need[w] & want) != want;
+        }
+        every = !__any(miss);
+    }
+    // next needed tile after i (ntiles if none)
+    auto next_tile = [&](int i) -> int {
+        if (every) return min(i + 1, ntiles);
+        for (int t = i + 1; t < ntiles; t = (t | 31) + 1) {
+            const uint32_t w = __builtin_amdgcn_readfirstlane(s_need[t >> 5]) >> (t & 31);
+            if (w) return min(t + __builtin_ctz(w), ntiles);
+        }
+        return ntiles;
+    };
+    const int it0 = SKIP ? next_tile(-1) : 0, it1 = SKIP ? next_tile(it0) : 1, it2 = SKIP ? next_tile(it1) : 2;
+    if (SKIP && it0 < ntiles && (it0 != 0 || it1 != 1)) {
+        // the rows skip tile 0 or 1: request the first two tiles they need
+        meta_load<D, WAVES>(m1, bt, pis, key_begin + it0 * kTileN, key_end, tid);
+        meta_load<D, WAVES>(m2, bt, pis, key_begin + it1 * kTileN, key_end, tid);
+        data_load<D, WAVES>(p, dnext, m1, g, key_begin + it0 * kTileN, key_end, tid, kV);
+        cs_load<D, WAVES>(p, dnext, tid);
+    }
+    if (SKIP ? it0 < ntiles : ntiles > 0) {
         (void)data_store<D, WAVES>(dnext, Ks, Vs, s_pi, tid, kV, min_pos, p.rotate_k != 0);
         __syncthreads();
     }
@@ -639,18 +696,19 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     };
 
     f32x4 sA[QG][2], sB[QG][2];
-    if (ntiles > 0) {
+    if (SKIP ? it0 < ntiles : ntiles > 0) {
         qk_half(Ks, 0, sA);
-        data_load<D, WAVES>(p, dnext, m2, g, key_begin + kTileN, key_end, tid, kV);
-        meta_load<D, WAVES>(m2, bt, pis, key_begin + 2 * kTileN, key_end, tid);
+        data_load<D, WAVES>(p, dnext, m2, g, key_begin + it1 * kTileN, key_end, tid, kV);
+        meta_load<D, WAVES>(m2, bt, pis, key_begin + it2 * kTileN, key_end, tid);
     }
 
-    // One tile; MORE: a next tile exists (stage it), FULL: no masking needed.
+    // One tile: the k-th processed, tile index it; n1, n2, n3 the next three
+    // needed tiles.  MORE: n1 exists (stage it), FULL: no masking needed.
     // Each region is straight-line code so the MFMA / VALU interleave hints
     // apply to it.
-    auto tile_body = [&](auto more_c, auto full_c, int it) {
+    auto tile_body = [&](auto more_c, auto full_c, int k, int it, int n1, int n2, int n3) {
         constexpr bool MORE = decltype(more_c)::value;
-        const int cur = it & 1;
+        const int cur = (SKIP ? k : it) & 1;
         const int tile = key_begin + it * kTileN;
         const uint16_t *Kc = Ks + cur * GG::KBUF;
         const uint16_t *Vc = Vs + (kV ? cur * GG::VBUF : 0);
@@ -717,12 +775,14 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
                     p.mass_part[(((size_t)r * p.hkv + g) * p.row_blocks + rb) * p.mass_stride + j] = tot;
             }
         }
-        // R4: QK(next tile, half 0) || request tile t+2
+        // R4: QK(next tile, half 0) || request the tile after it
         if constexpr (MORE) {
             qk_half(Ks + (cur ^ 1) * GG::KBUF, 0, sA);
-            data_load<D, WAVES>(p, dnext, m2, g, tile + 2 * kTileN, key_end, tid, kV);
-            meta_load<D, WAVES>(m2, bt, pis, tile + 3 * kTileN, key_end, tid);
+            data_load<D, WAVES>(p, dnext, m2, g, SKIP ? key_begin + n2 * kTileN : tile + 2 * kTileN, key_end, tid,
+                                kV);
+            meta_load<D, WAVES>(m2, bt, pis, SKIP ? key_begin + n3 * kTileN : tile + 3 * kTileN, key_end, tid);
         }
+        (void)n1;
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
@@ -731,13 +791,34 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     // allocation.  A partial last tile is always masked.
     const int t_split = first_bad == 0x7fffffff ? ntiles : (first_bad - key_begin) / kTileN;
     const bool last_partial = ntiles > 0 && key_end - (key_begin + (ntiles - 1) * kTileN) < kTileN;
-    const int nf = min(t_split, ntiles - 1);
-    int it = 0;
-    for (; it < nf; ++it) tile_body(T_{}, T_{}, it);
-    for (; it < ntiles - 1; ++it) tile_body(T_{}, F_{}, it);
-    if (ntiles > 0) {
-        if (t_split >= ntiles && !last_partial) tile_body(F_{}, T_{}, ntiles - 1);
-        else tile_body(F_{}, F_{}, ntiles - 1);
+    if constexpr (SKIP) {
+        // the needed tiles in order: (it, n1, n2) advance together
+        int k = 0, it = it0, n1 = it1, n2 = it2;
+        for (; n1 < ntiles && it < t_split; ++k) {
+            const int n3 = next_tile(n2);
+            tile_body(T_{}, T_{}, k, it, n1, n2, n3);
+            it = n1, n1 = n2, n2 = n3;
+        }
+        for (; n1 < ntiles; ++k) {
+            const int n3 = next_tile(n2);
+            tile_body(T_{}, F_{}, k, it, n1, n2, n3);
+            it = n1, n1 = n2, n2 = n3;
+        }
+        if (it < ntiles) {
+            if (it < t_split && !(it == ntiles - 1 && last_partial))
+                tile_body(F_{}, T_{}, k, it, ntiles, ntiles, ntiles);
+            else
+                tile_body(F_{}, F_{}, k, it, ntiles, ntiles, ntiles);
+        }
+    } else {
+        const int nf = min(t_split, ntiles - 1);
+        int it = 0;
+        for (; it < nf; ++it) tile_body(T_{}, T_{}, it, it, 0, 0, 0);
+        for (; it < ntiles - 1; ++it) tile_body(T_{}, F_{}, it, it, 0, 0, 0);
+        if (ntiles > 0) {
+            if (t_split >= ntiles && !last_partial) tile_body(F_{}, T_{}, ntiles - 1, ntiles - 1, 0, 0, 0);
+            else tile_body(F_{}, F_{}, ntiles - 1, ntiles - 1, 0, 0, 0);
+        }
     }
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) m_run[qg] = m_ref[qg];
@@ -1098,24 +1179,29 @@ __global__ __launch_bounds__(256) void merge_many_kernel(MergeParams p) {
     *reinterpret_cast<uint2 *>(p.out + (size_t)row * D + 4 * q4) = w;
 }
 
-template <int D, int QG, int WAVES, int MODE>
+template <int D, int QG, int WAVES, int MODE, bool SKIP>
 hipError_t launch_one(const FwdParams &p, hipStream_t s) {
     const int nwg = p.row_blocks * p.hkv * p.num_splits * p.batch;
     if (nwg <= 0) return hipSuccess;
     if constexpr (MODE == kMass && QG == 2)
         hipLaunchKernelGGL((mass_kernel<D, QG, WAVES>), dim3(nwg), dim3(64 * WAVES), 0, s, p);
     else
-        hipLaunchKernelGGL((fwd_kernel<D, QG, WAVES, MODE>), dim3(nwg), dim3(64 * WAVES), 0, s, p);
+        hipLaunchKernelGGL((fwd_kernel<D, QG, WAVES, MODE, SKIP>), dim3(nwg), dim3(64 * WAVES), 0, s, p);
     return hipGetLastError();
 }
 
 // Variants: shape 0 = (QG 1, 4 waves): 64 rows per workgroup; shape 1 =
-// (QG 2, 8 waves): 256 rows at d = 128, (QG 2, 4 waves): 128 rows at d = 64.
+// (QG 2, 8 waves): 256 rows at d = 128, (QG 2, 4 waves): 128 rows at d = 64;
+// shape 2 = shape 1 that skips tiles no row of the workgroup sees (not in
+// mass mode).
 template <int D, int MODE>
 hipError_t launch_shape(const FwdParams &p, int shape, hipStream_t s) {
-    if (shape == 0) return launch_one<D, 1, 4, MODE>(p, s);
-    if constexpr (D == 128) return launch_one<D, 2, 8, MODE>(p, s);
-    else return launch_one<D, 2, 4, MODE>(p, s);
+    constexpr bool S = MODE != kMass;
+    if (shape == 0) return launch_one<D, 1, 4, MODE, false>(p, s);
+    if constexpr (D == 128)
+        return shape == 2 ? launch_one<D, 2, 8, MODE, S>(p, s) : launch_one<D, 2, 8, MODE, false>(p, s);
+    else
+        return shape == 2 ? launch_one<D, 2, 4, MODE, S>(p, s) : launch_one<D, 2, 4, MODE, false>(p, s);
 }
 
 template <int D>
@@ -1129,7 +1215,7 @@ hipError_t launch_mode(const FwdParams &p, int mode, int shape, hipStream_t s) {
 
 }  // namespace
 
-int fwd_rows_per_block(int head_dim, int shape) { return shape == 0 ? 64 : (head_dim == 128 ? 256 : 128); }
+int fwd_rows_per_block(int head_dim, int shape) { return shape == 0 ? 64 : (head_dim == 128 ? 256 : 128); }   // 2 as 1
 
 hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int shape, hipStream_t s) {
     return head_dim == 64 ? launch_mode<64>(p, mode, shape, s) : launch_mode<128>(p, mode, shape, s);

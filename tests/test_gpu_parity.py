@@ -511,6 +511,27 @@ def test_recompute_full_size_sampled():
     assert np.max(np.abs(lse.cpu().numpy()[ts, hs] - ref_l)) <= LSE_ABS
 
 
+def test_recompute_skips_tiles_no_row_sees():
+    """Queries at scattered positions in more than 8 row blocks (the variant
+    that skips tiles no row of a workgroup sees), over a context whose
+    positions run backwards through the slots: row blocks early in position
+    order need only late tiles, so the first tile they stage is not tile 0."""
+    w = W.custom(112, Hq=8, Hkv=2, d=64, theta=1e4, span_lens=[[640, 512, 768, 384, 512]], q_len=[8])
+    n = int(w.kv_len[0]) - 8
+    ctx_slots = np.nonzero(w.kv_pos[0, :n] >= 0)[0]
+    top = int(w.kv_pos[0, ctx_slots].max())
+    w.kv_pos[0, ctx_slots] = top - w.kv_pos[0, ctx_slots]
+    rng = np.random.default_rng(113)
+    picked = np.sort(rng.choice(ctx_slots, size=845, replace=False))
+    wr = W.recompute_queries(w, [w.kv_pos[0, picked]], 114)
+    say(f"recompute skip: {wr.total_q} queries x {w.num_q_heads // w.num_kv_heads} heads per kv head")
+    ctx = H.ctx_for(wr)
+    out, lse, _ = H.prefill(ctx, wr)
+    ref_o, ref_l = oracle.attention(wr)
+    compare_out(H.host_bf16(out), ref_o, "O recompute skip")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+
+
 # ------------------------------------------- span reuse by block hashing
 
 def test_block_hash_reuse_end_to_end():
