@@ -1095,16 +1095,44 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     const int gtid = blockIdx.x * 256 + threadIdx.x;
     const int row = gtid / TPR, part = gtid % TPR;
     if (row >= p.rows) return;
-    float M = -INFINITY;
-    for (int s = 0; s < p.num_splits; ++s) M = fmaxf(M, p.part_ml[((size_t)s * p.rows + row) * 2]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float L = 0.f;
+    constexpr int kMax = 16;
+    const int S = p.num_splits;
+    float M = -INFINITY, L = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < p.num_splits; ++s) {
-        const size_t pr = (size_t)s * p.rows + row;
-        const float w = fast_exp2(p.part_ml[pr * 2] - Mu);
-        L += w * p.part_ml[pr * 2 + 1];
-        if (p.part_o) o += w * *reinterpret_cast<const f32x4 *>(p.part_o + pr * D + 4 * part);
+    if (S <= kMax) {
+        // the usual case: all of a thread's loads are issued before the sums,
+        // which run in split order
+        float2 ml[kMax];
+        f32x4 po[kMax];
+#pragma unroll
+        for (int s = 0; s < kMax; ++s) {
+            if (s < S) {
+                const size_t pr = (size_t)s * p.rows + row;
+                ml[s] = *reinterpret_cast<const float2 *>(p.part_ml + pr * 2);
+                if (p.part_o) po[s] = *reinterpret_cast<const f32x4 *>(p.part_o + pr * D + 4 * part);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < kMax; ++s)
+            if (s < S) M = fmaxf(M, ml[s].x);
+        const float Mu = M == -INFINITY ? 0.f : M;
+#pragma unroll
+        for (int s = 0; s < kMax; ++s) {
+            if (s < S) {
+                const float w = fast_exp2(ml[s].x - Mu);
+                L += w * ml[s].y;
+                if (p.part_o) o += w * po[s];
+            }
+        }
+    } else {
+        for (int s = 0; s < S; ++s) M = fmaxf(M, p.part_ml[((size_t)s * p.rows + row) * 2]);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        for (int s = 0; s < S; ++s) {
+            const size_t pr = (size_t)s * p.rows + row;
+            const float w = fast_exp2(p.part_ml[pr * 2] - Mu);
+            L += w * p.part_ml[pr * 2 + 1];
+            if (p.part_o) o += w * *reinterpret_cast<const f32x4 *>(p.part_o + pr * D + 4 * part);
+        }
     }
     const bool any = L > 0.f;
     if (p.out) {
