@@ -54,16 +54,8 @@ struct FwdPlan {
     int num_splits = 1;
 };
 
-FwdPlan plan_fwd(const pic_config &c, int batch, int max_q_len, int max_kv_len) {
-    FwdPlan pl;
-    const int G = c.num_q_heads / c.num_kv_heads;
-    const long long rows = (long long)max_q_len * G;
-    pl.shape = rows >= 128 ? 1 : 0;
-    pl.rows_per_block = pic::fwd_rows_per_block(c.head_dim, pl.shape);
-    pl.row_blocks = (int)((rows + pl.rows_per_block - 1) / pl.rows_per_block);
-    // many row blocks hold queries at many different positions: take the
-    // variant that skips the tiles no row of a workgroup sees
-    if (pl.shape == 1 && pl.row_blocks >= 8) pl.shape = 2;
+// Splits of the key range so that base workgroups x splits fill the GPU.
+void set_splits(FwdPlan &pl, const pic_config &c, int batch, int max_kv_len) {
     const long long base = (long long)pl.row_blocks * c.num_kv_heads * batch;
     // the big shape runs one 512-thread workgroup per CU, the small one several
     const long long target = pl.shape >= 1 && c.head_dim == 128 ? kCUs : 2 * kCUs;
@@ -76,6 +68,32 @@ FwdPlan plan_fwd(const pic_config &c, int batch, int max_q_len, int max_kv_len) 
     const int per = max_kv_len > 0 ? (max_kv_len + splits - 1) / splits : pic::kTileN;
     pl.split_len = std::max(pic::kTileN, (per + pic::kTileN - 1) / pic::kTileN * pic::kTileN);
     pl.num_splits = max_kv_len > 0 ? (max_kv_len + pl.split_len - 1) / pl.split_len : 1;
+}
+
+FwdPlan plan_fwd(const pic_config &c, int batch, int max_q_len, int max_kv_len) {
+    FwdPlan pl;
+    const int G = c.num_q_heads / c.num_kv_heads;
+    const long long rows = (long long)max_q_len * G;
+    pl.shape = rows >= 128 ? 1 : 0;
+    pl.rows_per_block = pic::fwd_rows_per_block(c.head_dim, pl.shape);
+    pl.row_blocks = (int)((rows + pl.rows_per_block - 1) / pl.rows_per_block);
+    // many row blocks hold queries at many different positions: take the
+    // variant that skips the tiles no row of a workgroup sees
+    if (pl.shape == 1 && pl.row_blocks >= 8) pl.shape = 2;
+    set_splits(pl, c, batch, max_kv_len);
+    return pl;
+}
+
+// The selection mass pass: at shape >= 1 its workgroups hold twice the rows
+// (4 row tiles per wave: it keeps no O accumulator), and it never skips tiles.
+FwdPlan plan_mass(const pic_config &c, int batch, int max_q_len, int max_kv_len) {
+    FwdPlan pl = plan_fwd(c, batch, max_q_len, max_kv_len);
+    if (pl.shape == 0) return pl;
+    const long long rows = (long long)max_q_len * (c.num_q_heads / c.num_kv_heads);
+    pl.shape = 1;
+    pl.rows_per_block = pic::mass_rows_per_block(c.head_dim);
+    pl.row_blocks = (int)((rows + pl.rows_per_block - 1) / pl.rows_per_block);
+    set_splits(pl, c, batch, max_kv_len);
     return pl;
 }
 
@@ -141,8 +159,8 @@ DecodeWs decode_ws(const pic_config &c, int batch, int splits) {
 struct SelectWs {
     size_t lse = 0, lse_ml = 0, mass_part = 0, mass = 0, total = 0;
 };
-SelectWs select_ws(const pic_config &c, const FwdPlan &pl, int batch, int max_blocks, int total_q,
-                   int max_kv_len) {
+SelectWs select_ws(const pic_config &c, const FwdPlan &pl, const FwdPlan &plm, int batch, int max_blocks,
+                   int total_q, int max_kv_len) {
     SelectWs w;
     size_t off = 0;
     const size_t rows = (size_t)total_q * c.num_q_heads;
@@ -151,7 +169,7 @@ SelectWs select_ws(const pic_config &c, const FwdPlan &pl, int batch, int max_bl
     w.lse_ml = off;
     if (pl.num_splits > 1) off += align_up((size_t)pl.num_splits * rows * 2 * sizeof(float));
     w.mass_part = off;
-    off += align_up((size_t)batch * c.num_kv_heads * pl.row_blocks * (size_t)max_kv_len * sizeof(float));
+    off += align_up((size_t)batch * c.num_kv_heads * plm.row_blocks * (size_t)max_kv_len * sizeof(float));
     w.mass = off;
     off += align_up((size_t)batch * max_blocks * kBlock * sizeof(float));
     w.total = off;
@@ -315,7 +333,8 @@ pic_status pic_workspace_bytes(const pic_ctx *ctx, pic_op op, const pic_req_tabl
     case PIC_OP_SELECT: {
         if (total_q < 0 || max_q_len < 0) return PIC_ERR_INVALID_ARG;
         const FwdPlan pl = plan_fwd(c, req->batch, max_q_len, req->max_kv_len);
-        *bytes = select_ws(c, pl, req->batch, req->max_blocks, total_q, req->max_kv_len).total;
+        const FwdPlan plm = plan_mass(c, req->batch, max_q_len, req->max_kv_len);
+        *bytes = select_ws(c, pl, plm, req->batch, req->max_blocks, total_q, req->max_kv_len).total;
         return PIC_OK;
     }
     case PIC_OP_ANCHOR:
@@ -446,7 +465,8 @@ pic_status qc_score_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
     if (req->batch == 0) return PIC_OK;
     const pic_config &c = ctx->cfg;
     const FwdPlan pl = plan_fwd(c, req->batch, qs->max_q_len, req->max_kv_len);
-    const SelectWs w = select_ws(c, pl, req->batch, req->max_blocks, qs->total_q, req->max_kv_len);
+    const FwdPlan plm = plan_mass(c, req->batch, qs->max_q_len, req->max_kv_len);
+    const SelectWs w = select_ws(c, pl, plm, req->batch, req->max_blocks, qs->total_q, req->max_kv_len);
     if (!ws || ws_bytes < w.total) return fail(ctx, PIC_ERR_WORKSPACE, "workspace too small for selection%s");
     hipStream_t s = (hipStream_t)stream;
     char *wb = (char *)ws;
@@ -475,11 +495,11 @@ pic_status qc_score_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
     std::memset(&sp, 0, sizeof sp);
     sp.mass_part = mass_part;
     sp.hkv = c.num_kv_heads;
-    sp.row_blocks = pl.row_blocks;
+    sp.row_blocks = plm.row_blocks;
     sp.mass_stride = req->max_kv_len;
     sp.q_start = qs->q_start;
     sp.group = c.num_q_heads / c.num_kv_heads;
-    sp.rows_per_block = pl.rows_per_block;
+    sp.rows_per_block = plm.rows_per_block;
     sp.kv_len = req->kv_len;
     sp.kv_pos = req->kv_pos;
     sp.kv_stride = req->max_blocks * kBlock;
@@ -497,7 +517,10 @@ pic_status qc_score_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
         pm.lse_in = lse_use;
         pm.mass_part = mass_part;
         pm.mass_stride = req->max_kv_len;
-        e = pic::launch_fwd(pm, c.head_dim, pic::kMass, pl.shape, s);
+        pm.split_len = plm.split_len;
+        pm.num_splits = plm.num_splits;
+        pm.row_blocks = plm.row_blocks;
+        e = pic::launch_fwd(pm, c.head_dim, pic::kMass, plm.shape, s);
         if (e != hipSuccess) return hip_fail(ctx, e, "selection mass launch");
     }
     e = pic::launch_mass_reduce(sp, s);

@@ -874,7 +874,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
 // attention kernel's.
 template <int D, int QG, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
-    static_assert(QG == 2, "the 32-row MFMA column sum packs two row tiles");
+    static_assert(QG % 2 == 0, "the 32-row MFMA column sum packs pairs of row tiles");
     using GG = Geo<D, WAVES>;
     constexpr int BM = 16 * QG * WAVES;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * GG::KBUF];
@@ -1020,22 +1020,29 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
         for (int T = 0; T < 2; ++T) {
             int kp = 0;
             if constexpr (!FULL) kp = pib[32 * kh + 8 * (lc >> 2) + 4 * T + (lc & 3)];
-            u32x4 pb;
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int qg = 0; qg < QG; ++qg)
+            for (int q2 = 0; q2 < QG; q2 += 2) {
+                // two row tiles make one 32-row B operand
+                u32x4 pb;
 #pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    float pr[2];
+                for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int i = 2 * h2 + e;
-                        float x = fmaf(sacc[qg][T][i], sc, -lse2[qg][i]);
-                        if constexpr (!FULL) x = kp <= rpos[qg][i] ? x : -INFINITY;
-                        pr[e] = fast_exp2(x);
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int qg = q2 + qq;
+                        float pr[2];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int i = 2 * h2 + e;
+                            float x = fmaf(sacc[qg][T][i], sc, -lse2[qg][i]);
+                            if constexpr (!FULL) x = kp <= rpos[qg][i] ? x : -INFINITY;
+                            pr[e] = fast_exp2(x);
+                        }
+                        pb[2 * qq + h2] = pack2(pr[0], pr[1]);
                     }
-                    pb[2 * qg + h2] = pack2(pr[0], pr[1]);
-                }
-            ds[T] = mfma16(ones_a, pb, f32x4{0.f, 0.f, 0.f, 0.f});
+                d = mfma16(ones_a, pb, d);
+            }
+            ds[T] = d;
         }
     };
     auto tile_body = [&](auto more_c, auto full_c, int it) {
@@ -1211,7 +1218,7 @@ template <int D, int QG, int WAVES, int MODE, bool SKIP>
 hipError_t launch_one(const FwdParams &p, hipStream_t s) {
     const int nwg = p.row_blocks * p.hkv * p.num_splits * p.batch;
     if (nwg <= 0) return hipSuccess;
-    if constexpr (MODE == kMass && QG == 2)
+    if constexpr (MODE == kMass && QG % 2 == 0)
         hipLaunchKernelGGL((mass_kernel<D, QG, WAVES>), dim3(nwg), dim3(64 * WAVES), 0, s, p);
     else
         hipLaunchKernelGGL((fwd_kernel<D, QG, WAVES, MODE, SKIP>), dim3(nwg), dim3(64 * WAVES), 0, s, p);
@@ -1226,6 +1233,8 @@ template <int D, int MODE>
 hipError_t launch_shape(const FwdParams &p, int shape, hipStream_t s) {
     constexpr bool S = MODE != kMass;
     if (shape == 0) return launch_one<D, 1, 4, MODE, false>(p, s);
+    // the mass pass of larger requests: QG 4 (mass_rows_per_block rows)
+    if constexpr (MODE == kMass) return launch_one<D, 4, D == 128 ? 8 : 4, MODE, false>(p, s);
     if constexpr (D == 128)
         return shape == 2 ? launch_one<D, 2, 8, MODE, S>(p, s) : launch_one<D, 2, 8, MODE, false>(p, s);
     else
@@ -1244,6 +1253,7 @@ hipError_t launch_mode(const FwdParams &p, int mode, int shape, hipStream_t s) {
 }  // namespace
 
 int fwd_rows_per_block(int head_dim, int shape) { return shape == 0 ? 64 : (head_dim == 128 ? 256 : 128); }   // 2 as 1
+int mass_rows_per_block(int head_dim) { return head_dim == 128 ? 512 : 256; }
 
 hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int shape, hipStream_t s) {
     return head_dim == 64 ? launch_mode<64>(p, mode, shape, s) : launch_mode<128>(p, mode, shape, s);
