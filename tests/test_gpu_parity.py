@@ -119,12 +119,20 @@ def test_prefill_full_size_sampled(name):
 
 # ---------------------------------------------------------------- decode
 
-@pytest.mark.parametrize("name", ["small", "small_private", "edge_g8"])
+@pytest.mark.parametrize("name", ["small", "small_private", "edge_g8", "d64", "d64_irregular"])
 def test_decode_parity(name):
     if name == "small":
         w = W.decode_heavy(batch=5, n_spans=3, span_tok=80)
     elif name == "small_private":
         w = W.decode_heavy(batch=3, n_spans=2, span_tok=1024, private_spans=True, Hq=32)
+    elif name.startswith("d64"):
+        w = W.custom(116, Hq=8, Hkv=2, d=64, theta=1e4, span_lens=[[300, 45], [1000], [2]],
+                     gaps=[[0, 7], [3], [0]], q_len=[1, 1, 1], decode=True)
+        if name == "d64_irregular":
+            # positions shuffled inside every other block of request 1
+            rng = np.random.default_rng(117)
+            for b in range(0, 1000 // 16, 2):
+                w.kv_pos[1, 16 * b:16 * b + 16] = rng.permutation(w.kv_pos[1, 16 * b:16 * b + 16])
     else:
         w = W.custom(109, Hq=16, Hkv=2, d=128, theta=5e5, span_lens=[[2500, 3], [1], [700, 700]],
                      gaps=[[0, 9], [3], [0, 0]], q_len=[1, 1, 1], decode=True)
@@ -230,6 +238,9 @@ def small_select_workloads():
         # spans longer than the 2048 slots the top-k keeps in registers
         "long_spans": lambda: W.custom(111, Hq=8, Hkv=2, d=64, theta=1e4, span_lens=[[3000, 5], [2049, 2048]],
                                        q_len=[8, 4], ratio=0.2),
+        # d = 64 with 160 rows per kv head: the 4-row-tile mass pass at d = 64
+        "d64_many_rows": lambda: W.custom(115, Hq=8, Hkv=2, d=64, theta=1e4, span_lens=[[300, 200], [150]],
+                                          q_len=[40, 33], ratio=0.2),
     }
 
 
