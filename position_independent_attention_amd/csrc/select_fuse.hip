@@ -201,11 +201,15 @@ __global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
         if (p.sel_off[s] + i < p.max_sel) out[i] = -1;
 }
 
-// One workgroup per (fused block fb, kv head g, request r).
+// One workgroup per (fused block fb, request r), over every kv head: fresh
+// K rows are copied 16 bytes at a time; fresh V rows are staged in LDS with
+// 16-byte loads and written channel-major, 8 slots (16 bytes) per store.
+// Only the fresh slots of a partial last block are written.
 template <int D>
 __global__ __launch_bounds__(256) void fuse_kernel(FuseParams p) {
-    __shared__ uint16_t s_v[16][D + 2];
-    const int fb = blockIdx.x, g = blockIdx.y, r = blockIdx.z, tid = threadIdx.x;
+    constexpr int CPR = D / 8;   // 16-byte chunks per row
+    __shared__ __attribute__((aligned(16))) uint16_t s_v[kBlock][D + 8];
+    const int fb = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
     const int row0 = max(0, p.sel_req_off[r]);
     const int cnt = min(p.sel_req_off[r + 1], p.n_sel) - row0;
     const int kv_stride = p.max_blocks * kBlock;
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseParams p) {
     kvl = kvl < 0 ? 0 : (kvl > kv_stride ? kv_stride : kvl);
     const int base = (kvl + kBlock - 1) / kBlock * kBlock;
     int32_t *pis = p.kv_pos + (size_t)r * kv_stride;
-    if (fb == 0 && g == 0) {
+    if (fb == 0) {
         for (int j = kvl + tid; j < base; j += 256) pis[j] = -1;
     }
     const int n_here = min(kBlock, cnt - kBlock * fb);
@@ -224,26 +228,42 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseParams p) {
     if (blk < 0 || blk >= p.num_blocks) return;
     const int rowb = row0 + kBlock * fb;
 
-    // K rows: token-major in the pool, 8 channels per task
-    for (int t = tid; t < kBlock * (D / 8); t += 256) {
-        const int sl = t / (D / 8), c = t % (D / 8);
-        if (sl < n_here) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(p.k_new + ((size_t)(rowb + sl) * p.hkv + g) * D + 8 * c);
-            *reinterpret_cast<u32x4 *>(p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + sl) * D + 8 * c) = v;
+    for (int g = 0; g < p.hkv; ++g) {
+        // K rows: token-major in the pool
+        for (int t = tid; t < kBlock * CPR; t += 256) {
+            const int sl = t / CPR, c = t % CPR;
+            if (sl < n_here) {
+                const u32x4 v =
+                    *reinterpret_cast<const u32x4 *>(p.k_new + ((size_t)(rowb + sl) * p.hkv + g) * D + 8 * c);
+                *reinterpret_cast<u32x4 *>(p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + sl) * D + 8 * c) = v;
+            }
         }
-    }
-    // V rows: stage token-major, write channel-major
-    for (int t = tid; t < kBlock * D; t += 256) {
-        const int sl = t / D, d = t % D;
-        s_v[sl][d] = sl < n_here ? p.v_new[((size_t)(rowb + sl) * p.hkv + g) * D + d] : (uint16_t)0;
-    }
-    __syncthreads();
-    for (int t = tid; t < kBlock * D; t += 256) {
-        const int d = t / kBlock, sl = t % kBlock;
-        if (sl < n_here) p.v_pool[(((size_t)blk * p.hkv + g) * D + d) * kBlock + sl] = s_v[sl][d];
+        // V rows: stage token-major ...
+        for (int t = tid; t < kBlock * CPR; t += 256) {
+            const int sl = t / CPR, c = t % CPR;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (sl < n_here) v = *reinterpret_cast<const u32x4 *>(p.v_new + ((size_t)(rowb + sl) * p.hkv + g) * D + 8 * c);
+            *reinterpret_cast<u32x4 *>(&s_v[sl][8 * c]) = v;
+        }
+        __syncthreads();
+        // ... and write channel-major: thread -> (channel d, slots 8h .. 8h+7)
+        for (int t = tid; t < 2 * D; t += 256) {
+            const int d = t >> 1, h = t & 1;
+            uint16_t *dst = p.v_pool + (((size_t)blk * p.hkv + g) * D + d) * kBlock + 8 * h;
+            if (8 * h + 8 <= n_here) {
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = (uint32_t)s_v[8 * h + 2 * e][d] | ((uint32_t)s_v[8 * h + 2 * e + 1][d] << 16);
+                *reinterpret_cast<u32x4 *>(dst) = w;
+            } else {
+                for (int i = 0; i < 8 && 8 * h + i < n_here; ++i) dst[i] = s_v[8 * h + i][d];
+            }
+        }
+        __syncthreads();
     }
     // positions: fresh slot takes the stale slot's pi, the stale slot is masked
-    if (g == 0 && tid < n_here) {
+    if (tid < n_here) {
         const int i = kBlock * fb + tid;
         const int sel = p.sel_idx[row0 + i];
         const int slot = base + i;
@@ -340,7 +360,7 @@ hipError_t launch_topk(const SelectParams &p, hipStream_t s) {
 hipError_t launch_fuse(const FuseParams &p, int head_dim, hipStream_t s) {
     if (p.batch <= 0) return hipSuccess;
     const int nfb = p.max_rows > 0 ? (p.max_rows + kBlock - 1) / kBlock : 1;
-    const dim3 grid(nfb, p.hkv, p.batch);
+    const dim3 grid(nfb, p.batch);
     if (head_dim == 64)
         hipLaunchKernelGGL(fuse_kernel<64>, grid, dim3(256), 0, s, p);
     else
