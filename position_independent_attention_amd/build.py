@@ -6,7 +6,8 @@ Each translation unit is compiled to an object in _build/ and linked into
 position_independent_attention_amd/libpicattn.so.  Flags: -O3, C++17,
 --offload-arch=gfx950, and the packed-fp32 target feature switched off for the
 device code (hipcc's host pass warns that it does not know the feature);
--fno-honor-nans for the kernel sources.
+-fno-honor-nans for the kernel sources; no edge splitting for machine sinking in
+the prefill / selection kernels.
 """
 from __future__ import annotations
 
@@ -34,11 +35,21 @@ CFLAGS = [
 # +-inf as sentinels but never rely on NaN semantics).  Host code keeps full
 # IEEE semantics for argument validation.
 KERNEL_FLAGS = ["-fno-honor-nans"]
+# The prefill / selection kernels: do not split a rarely taken branch's edge
+# to sink work into it.  The tile loop's rare paths (a moved softmax
+# reference) would otherwise pull the common path's exp2 out of the region
+# where it runs beside the MFMAs.
+FILE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-machine-sink-split=0"]}
+
+
+def flags_for(src: str) -> list:
+    """Extra hipcc flags for one source file."""
+    return (KERNEL_FLAGS if src.endswith(".hip") else []) + FILE_FLAGS.get(src, [])
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    extra = KERNEL_FLAGS if src.endswith(".hip") else []
+    extra = flags_for(src)
     cmd = [HIPCC] + CFLAGS + extra + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)

@@ -270,10 +270,10 @@ __device__ __forceinline__ void data_load(const FwdParams &p, Data<D, WAVES> &dt
 }
 
 // cos/sin rows of the staged keys (row 0 for unusable keys, whose data is 0).
-template <int D, int WAVES>
+template <int D, int WAVES, bool ROT>
 __device__ __forceinline__ void cs_load(const FwdParams &p, Data<D, WAVES> &dt, int tid) {
     using GG = Geo<D, WAVES>;
-    if (!p.rotate_k) return;   // keys stored rotated: no table rows
+    if constexpr (!ROT) return;   // keys stored rotated: no table rows
 #pragma unroll
     for (int u = 0; u < GG::KTASK; ++u) {
         const int pc = tid % GG::PC;
@@ -320,9 +320,9 @@ __device__ __forceinline__ int first_bad_key(const FwdParams &p, const int32_t *
 
 // Rotate and write one tile into an LDS buffer.  Returns whether every key
 // this thread staged is usable and visible to the workgroup's earliest row.
-template <int D, int WAVES>
+template <int D, int WAVES, bool ROT>
 __device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uint16_t *Vs, int32_t *s_pi, int tid,
-                                           bool need_v, int min_pos, bool rot) {
+                                           bool need_v, int min_pos) {
     using GG = Geo<D, WAVES>;
     bool full = true;
 #pragma unroll
@@ -331,7 +331,7 @@ __device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uin
         const int pc = tid % GG::PC;
         const int pi = dt.kpi[u];
         u32x4 lo = dt.klo[u], hi = dt.khi[u];
-        if (rot) rope8(lo, hi, dt.cs[u][0], dt.cs[u][1], dt.cs[u][2], dt.cs[u][3]);
+        if constexpr (ROT) rope8(lo, hi, dt.cs[u][0], dt.cs[u][1], dt.cs[u][2], dt.cs[u][3]);
         const int kr = krow(kk);
         *reinterpret_cast<u32x4 *>(Ks + koff<D>(kr, pc)) = lo;
         *reinterpret_cast<u32x4 *>(Ks + koff<D>(kr, GG::PC + pc)) = hi;
@@ -368,7 +368,7 @@ __device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uin
 
 // SKIP: skip the tiles whose keys no row of the workgroup sees (launched for
 // requests with many row blocks, whose positions differ from block to block).
-template <int D, int QG, int WAVES, int MODE, bool SKIP>
+template <int D, int QG, int WAVES, int MODE, bool SKIP, bool ROT>
 __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     using GG = Geo<D, WAVES>;
     constexpr int BM = 16 * QG * WAVES;
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end, tid);
         meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
         data_load<D, WAVES>(p, dnext, m1, g, key_begin, key_end, tid, kV);
-        cs_load<D, WAVES>(p, dnext, tid);
+        cs_load<D, WAVES, ROT>(p, dnext, tid);
     }
     __syncthreads();
     const int min_pos = s_minpos;
@@ -543,10 +543,10 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         meta_load<D, WAVES>(m1, bt, pis, key_begin + it0 * kTileN, key_end, tid);
         meta_load<D, WAVES>(m2, bt, pis, key_begin + it1 * kTileN, key_end, tid);
         data_load<D, WAVES>(p, dnext, m1, g, key_begin + it0 * kTileN, key_end, tid, kV);
-        cs_load<D, WAVES>(p, dnext, tid);
+        cs_load<D, WAVES, ROT>(p, dnext, tid);
     }
     if (SKIP ? it0 < ntiles : ntiles > 0) {
-        (void)data_store<D, WAVES>(dnext, Ks, Vs, s_pi, tid, kV, min_pos, p.rotate_k != 0);
+        (void)data_store<D, WAVES, ROT>(dnext, Ks, Vs, s_pi, tid, kV, min_pos);
         __syncthreads();
     }
     const float sc = p.scale_log2;
@@ -651,48 +651,29 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
             for (int dt = 0; dt < D / 16; ++dt) acc[qg][dt] *= alpha;
         }
     };
-    // Decide the next reference after a half whose lane-local raw maxima are
-    // mx.  Only when some lane passed the reference by more than the slack are
-    // the column maxima formed (wave-uniform branch); if one jumped past the
-    // fp32-safe range, rescale now and recompute that half's P.
+    // After a half whose lane-local raw maxima are mx: only when some lane
+    // passed the reference by more than the slack (wave-uniform branch, rare
+    // once the first keys are seen) are the column maxima formed; columns
+    // whose maximum passed it move their reference there, the accumulators
+    // follow at once (nothing of this half is in them yet) and the half's P
+    // is formed again against the new reference.  The common path is one
+    // compare per column and no branch target inside the MFMA / VALU regions.
     auto settle = [&](auto full_c, const f32x4 (&sacc)[QG][2], const int32_t *pib, int kh, u32x4 (&pb)[QG],
-                      const float (&mx)[QG], float (&m_next)[QG], float (&cs)[16]) {
+                      const float (&mx)[QG], float (&cs)[16]) {
         bool need = false;
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-            m_next[qg] = m_ref[qg];
-            need = need || mx[qg] * sc > m_ref[qg] + kRescaleSlack;
-        }
+        for (int qg = 0; qg < QG; ++qg) need = need || mx[qg] * sc > m_ref[qg] + kRescaleSlack;
         if (__any(need)) {
-            bool big = false;
+            float mx2[QG];
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) {
                 const float cm = col_max(mx[qg]) * sc;
-                m_next[qg] = cm > m_ref[qg] + kRescaleSlack ? cm : m_ref[qg];
-                big = big || cm > m_ref[qg] + 64.f;
+                const float m_new = cm > m_ref[qg] + kRescaleSlack ? cm : m_ref[qg];
+                rescale(qg, m_ref[qg], m_new);
+                m_ref[qg] = m_new;
             }
-            if (__any(big)) {
-                float mx2[QG];
-#pragma unroll
-                for (int qg = 0; qg < QG; ++qg) {
-                    rescale(qg, m_ref[qg], m_next[qg]);
-                    m_ref[qg] = m_next[qg];
-                }
-                softmax_half(full_c, sacc, pib, kh, pb, mx2, cs);
-            }
+            softmax_half(full_c, sacc, pib, kh, pb, mx2, cs);
         }
-    };
-    // After a half's PV: move the accumulators to the new reference.
-    auto commit = [&](const float (&m_next)[QG]) {
-        bool moved = false;
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) moved = moved || m_next[qg] != m_ref[qg];
-        if (__any(moved)) {
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) rescale(qg, m_ref[qg], m_next[qg]);
-        }
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) m_ref[qg] = m_next[qg];
     };
 
     f32x4 sA[QG][2], sB[QG][2];
@@ -714,7 +695,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         const uint16_t *Vc = Vs + (kV ? cur * GG::VBUF : 0);
         const int32_t *pc_ = s_pi + cur * kTileN;
         u32x4 pb0[QG], pb1[QG];
-        float mx0[QG], mx1[QG], mn0[QG], mn1[QG];
+        float mx0[QG], mx1[QG];
         float cs[16];   // kMass: column sums of this lane's 16 keys
 #pragma unroll
         for (int u = 0; u < 16; ++u) cs[u] = 0.f;
@@ -723,16 +704,15 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         qk_half(Kc, 1, sB);
         softmax_half(full_c, sA, pc_, 0, pb0, mx0, cs);
         interleave_hint<2 * QG * GG::NC, 4>();
-        if constexpr (MODE != kMass) settle(full_c, sA, pc_, 0, pb0, mx0, mn0, cs);
+        if constexpr (MODE != kMass) settle(full_c, sA, pc_, 0, pb0, mx0, cs);
 
         // R2: PV(half 0) || softmax(half 1)
         pv_half(Vc, 0, pb0);
-        if constexpr (MORE) cs_load<D, WAVES>(p, dnext, tid);
+        if constexpr (MORE) cs_load<D, WAVES, ROT>(p, dnext, tid);
         softmax_half(full_c, sB, pc_, 1, pb1, mx1, cs);
         if constexpr (MODE != kMass) {
             interleave_hint<QG * (D / 16 + 1), 4>();
-            commit(mn0);
-            settle(full_c, sB, pc_, 1, pb1, mx1, mn1, cs);
+            settle(full_c, sB, pc_, 1, pb1, mx1, cs);
         }
 
         // R3: PV(half 1) || rotate + stage the next tile
@@ -755,12 +735,9 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         }
         bool f = true;
         if constexpr (MORE)
-            f = data_store<D, WAVES>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs + (kV ? (cur ^ 1) * GG::VBUF : 0),
-                                     s_pi + (cur ^ 1) * kTileN, tid, kV, min_pos, p.rotate_k != 0);
-        if constexpr (MODE != kMass) {
-            interleave_hint<QG * (D / 16 + 1), 3>();
-            commit(mn1);
-        }
+            f = data_store<D, WAVES, ROT>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs + (kV ? (cur ^ 1) * GG::VBUF : 0),
+                                     s_pi + (cur ^ 1) * kTileN, tid, kV, min_pos);
+        if constexpr (MODE != kMass) interleave_hint<QG * (D / 16 + 1), 3>();
         (void)f;
         __syncthreads();
 
@@ -872,7 +849,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
 // against an A operand whose row 0 is ones: no cross-lane reduction.  The
 // staging (tile loads two ahead, rotation, LDS double buffer) is the
 // attention kernel's.
-template <int D, int QG, int WAVES>
+template <int D, int QG, int WAVES, bool ROT>
 __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
     static_assert(QG % 2 == 0, "the 32-row MFMA column sum packs pairs of row tiles");
     using GG = Geo<D, WAVES>;
@@ -978,7 +955,7 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
         meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end, tid);
         meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
         data_load<D, WAVES>(p, dnext, m1, g, key_begin, key_end, tid, false);
-        cs_load<D, WAVES>(p, dnext, tid);
+        cs_load<D, WAVES, ROT>(p, dnext, tid);
     }
     __syncthreads();
     const int min_pos = s_minpos;
@@ -989,7 +966,7 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
     __syncthreads();
     const int first_bad = s_firstbad;
     if (ntiles > 0) {
-        (void)data_store<D, WAVES>(dnext, Ks, Vs, s_pi, tid, false, min_pos, p.rotate_k != 0);
+        (void)data_store<D, WAVES, ROT>(dnext, Ks, Vs, s_pi, tid, false, min_pos);
         __syncthreads();
         data_load<D, WAVES>(p, dnext, m2, g, key_begin + kTileN, key_end, tid, false);
         meta_load<D, WAVES>(m2, bt, pis, key_begin + 2 * kTileN, key_end, tid);
@@ -1055,7 +1032,7 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
         qk(Kc, 0, sA);
         qk(Kc, 1, sB);
         colsum(full_c, sA, pc_, 0, d0);
-        if constexpr (MORE) cs_load<D, WAVES>(p, dnext, tid);
+        if constexpr (MORE) cs_load<D, WAVES, ROT>(p, dnext, tid);
         colsum(full_c, sB, pc_, 1, d1);
         if (lg == 0) {
 #pragma unroll
@@ -1066,8 +1043,8 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
             }
         }
         if constexpr (MORE)
-            (void)data_store<D, WAVES>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs, s_pi + (cur ^ 1) * kTileN, tid, false,
-                                       min_pos, p.rotate_k != 0);
+            (void)data_store<D, WAVES, ROT>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs, s_pi + (cur ^ 1) * kTileN, tid, false,
+                                       min_pos);
         __syncthreads();
         if (tid < kTileN) {
             float tot = 0.f;
@@ -1214,14 +1191,22 @@ __global__ __launch_bounds__(256) void merge_many_kernel(MergeParams p) {
     *reinterpret_cast<uint2 *>(p.out + (size_t)row * D + 4 * q4) = w;
 }
 
+// ROT: keys are rotated at pi while staged (the method's path); without it
+// the pool holds keys already rotated at their positions (ablation mode) and
+// no table row is read.  A compile-time choice, so that no branch splits the
+// MFMA / VALU regions of the tile loop.
 template <int D, int QG, int WAVES, int MODE, bool SKIP>
 hipError_t launch_one(const FwdParams &p, hipStream_t s) {
     const int nwg = p.row_blocks * p.hkv * p.num_splits * p.batch;
     if (nwg <= 0) return hipSuccess;
-    if constexpr (MODE == kMass && QG % 2 == 0)
-        hipLaunchKernelGGL((mass_kernel<D, QG, WAVES>), dim3(nwg), dim3(64 * WAVES), 0, s, p);
-    else
-        hipLaunchKernelGGL((fwd_kernel<D, QG, WAVES, MODE, SKIP>), dim3(nwg), dim3(64 * WAVES), 0, s, p);
+    const dim3 grid(nwg), block(64 * WAVES);
+    if constexpr (MODE == kMass && QG % 2 == 0) {
+        if (p.rotate_k) hipLaunchKernelGGL((mass_kernel<D, QG, WAVES, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((mass_kernel<D, QG, WAVES, false>), grid, block, 0, s, p);
+    } else {
+        if (p.rotate_k) hipLaunchKernelGGL((fwd_kernel<D, QG, WAVES, MODE, SKIP, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((fwd_kernel<D, QG, WAVES, MODE, SKIP, false>), grid, block, 0, s, p);
+    }
     return hipGetLastError();
 }
 
@@ -1235,7 +1220,7 @@ hipError_t launch_shape(const FwdParams &p, int shape, hipStream_t s) {
     if (shape == 0) return launch_one<D, 1, 4, MODE, false>(p, s);
     // the mass pass of larger requests: QG 4 (mass_rows_per_block rows)
     if constexpr (MODE == kMass) return launch_one<D, 4, D == 128 ? 8 : 4, MODE, false>(p, s);
-    if constexpr (D == 128)
+    else if constexpr (D == 128)
         return shape == 2 ? launch_one<D, 2, 8, MODE, S>(p, s) : launch_one<D, 2, 8, MODE, false>(p, s);
     else
         return shape == 2 ? launch_one<D, 2, 4, MODE, S>(p, s) : launch_one<D, 2, 4, MODE, false>(p, s);

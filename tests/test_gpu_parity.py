@@ -95,6 +95,55 @@ def test_prefill_row_without_visible_keys():
     compare_out(o, ref_o, "O")
 
 
+def score_jumps(decode=False):
+    """Keys placed so that one (query, head) row each scores 10 to 24 log2
+    units above everything it has seen before, at slots past the first tiles
+    (the start and the middle of 64-key tiles and 16-key blocks): the
+    softmax reference of those rows moves after keys were already
+    accumulated.  Each key is c * R(pos - pi) q for its row's query q, i.e.
+    after rotation it points along the rotated query; c sets the score."""
+    w = W.custom(118, Hq=8, Hkv=2, d=128, theta=5e5, span_lens=[[1000], [300, 400]],
+                 q_len=[1, 1] if decode else [40, 9], decode=decode)
+    d, G = w.head_dim, w.num_q_heads // w.num_kv_heads
+    sc = np.log2(np.e) / np.sqrt(d)
+    k = W.bf16_bits_to_f32(w.pool_k)
+    # (request, key slot, query row in the request, head, score in log2 units)
+    for r, j, tt, h, jump in [(0, 194, 0, 0, 12.), (0, 385, 5, 3, 16.), (0, 609, 11, 5, 20.), (0, 800, 39, 6, 24.),
+                              (0, 450, 20, 1, 10.), (1, 130, 0, 2, 12.), (1, 322, 3, 7, 18.), (1, 512, 8, 4, 22.)]:
+        t = int(w.q_start[r]) + (0 if decode else tt)
+        q = W.bf16_bits_to_f32(w.q[t, h]).astype(np.float64)
+        turn = int(w.q_pos[t]) - int(w.kv_pos[r, j])
+        k[w.block_table[r, j // 16], h // G, j % 16, :] = jump / sc / np.dot(q, q) * oracle.rope(d, w.rope_theta, turn, q)
+    w.pool_k = W.f32_to_bf16_bits(k)
+    return w
+
+
+@pytest.mark.parametrize("op", ["prefill", "decode"])
+def test_score_jumps_move_the_softmax_reference(op):
+    """Bar: O as everywhere; LSE per row within the worst-case effect of the
+    bf16 rounding of the rotated q and k (relative 2^-9 each) on any score,
+    2^-8 |q| max_j |k_j| / sqrt(d) by Cauchy-Schwarz, plus 2^-8 for the
+    bf16 probabilities.  A reference mix-up is off by 2^8 or more in the
+    weights, i.e. by order |V| in O and 5 or more in the LSE."""
+    w = score_jumps(decode=op == "decode")
+    ctx = H.ctx_for(w)
+    out, lse, _ = H.prefill(ctx, w) if op == "prefill" else H.decode(ctx, w)
+    ref_o, ref_l = oracle.attention(w)
+    say(f"{op} score jumps: lse range {ref_l.min():.1f} .. {ref_l.max():.1f}")
+    compare_out(H.host_bf16(out), ref_o, "O")
+    G = w.num_q_heads // w.num_kv_heads
+    qn = np.linalg.norm(W.bf16_bits_to_f32(w.q).astype(np.float64), axis=-1)             # [t][h]
+    kn = np.linalg.norm(W.bf16_bits_to_f32(w.pool_k).astype(np.float64), axis=-1)        # [blk][g][slot]
+    err = np.abs(lse.cpu().numpy() - ref_l)
+    for r in range(w.batch):
+        blocks = w.block_table[r, :(int(w.kv_len[r]) + 15) // 16]
+        kmax = kn[blocks].max(axis=(0, 2))                                               # [g]
+        for t in range(int(w.q_start[r]), int(w.q_start[r + 1])):
+            bound = 2.0 ** -8 * qn[t] * np.repeat(kmax, G) / np.sqrt(w.head_dim) + 2.0 ** -8
+            assert np.all(err[t] <= bound), (t, err[t], bound)
+    say(f"  LSE: max {err.max():.3e}")
+
+
 @pytest.mark.parametrize("name", ["shared_serving", "long_context"])
 def test_prefill_full_size_sampled(name):
     w = {"shared_serving": W.shared_serving, "long_context": W.long_context}[name]()
