@@ -286,6 +286,29 @@ __device__ __forceinline__ void cs_load(const FwdParams &p, Data<D, WAVES> &dt, 
     }
 }
 
+// Positions and block ids of the first two steps of first_bad_key, requested
+// before the workgroup's earliest position is known.
+struct FbPre {
+    i32x4 pi[2];
+    int32_t blk[2];
+};
+
+// Steps past the range read index 0 (every request row has a first block);
+// those values are not used.
+template <int NT>
+__device__ __forceinline__ FbPre fb_preload(const int32_t *bt, const int32_t *pis, int key_begin, int key_end,
+                                            int tid) {
+    FbPre f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int j0 = key_begin + 4 * tid + 4 * NT * s;
+        const int jc = j0 < key_end ? j0 : 0;
+        f.pi[s] = *reinterpret_cast<const i32x4 *>(pis + jc);
+        f.blk[s] = bt[jc >> 4];
+    }
+    return f;
+}
+
 // First key of [key_begin, key_end) that is unusable or not visible to the
 // row with the smallest position (INT_MAX if none).  Four keys per thread and
 // step with no early exit, so the loads of all steps can be in flight at once.
@@ -293,15 +316,13 @@ __device__ __forceinline__ void cs_load(const FwdParams &p, Data<D, WAVES> &dt, 
 // aligned and stays inside the request's position row.  With s_need, also
 // sets bit t of s_need for every 64-key tile t holding a usable key that the
 // row with the largest position (max_row) sees.
+// The first two steps use the rows preloaded by fb_preload.
 template <int NT>
-__device__ __forceinline__ int first_bad_key(const FwdParams &p, const int32_t *bt, const int32_t *pis, int key_begin,
-                                             int key_end, int min_pos, int tid, int max_row = -1,
-                                             uint32_t *s_need = nullptr) {
+__device__ __forceinline__ int first_bad_key(const FwdParams &p, const int32_t *bt, const int32_t *pis,
+                                             const FbPre &pre, int key_begin, int key_end, int min_pos, int tid,
+                                             int max_row = -1, uint32_t *s_need = nullptr) {
     int bad = 0x7fffffff;
-#pragma unroll 4
-    for (int j0 = key_begin + 4 * tid; j0 < key_end; j0 += 4 * NT) {
-        const i32x4 pi = *reinterpret_cast<const i32x4 *>(pis + j0);
-        const int blk = bt[j0 >> 4];
+    auto step = [&](int j0, const i32x4 pi, int blk) {
         const bool bok = blk >= 0 && blk < p.num_blocks;
         bool need = false;
 #pragma unroll
@@ -314,7 +335,15 @@ __device__ __forceinline__ int first_bad_key(const FwdParams &p, const int32_t *
             const int t = (j0 - key_begin) >> 6;   // the 4 keys share a tile
             atomicOr(&s_need[t >> 5], 1u << (t & 31));
         }
+    };
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int j0 = key_begin + 4 * tid + 4 * NT * s;
+        if (j0 < key_end) step(j0, pre.pi[s], pre.blk[s]);
     }
+#pragma unroll 4
+    for (int j0 = key_begin + 4 * tid + 8 * NT; j0 < key_end; j0 += 4 * NT)
+        step(j0, *reinterpret_cast<const i32x4 *>(pis + j0), bt[j0 >> 4]);
     return bad;
 }
 
@@ -414,6 +443,19 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     if constexpr (SKIP)
         for (int w = tid; w < kNeedWords; w += GG::NT) s_need[w] = 0u;
 
+    // ---- requests that need nothing from the rows go first: block ids and
+    // positions of tiles 0 and 1 and of the first-unusable-key scan.  Tile
+    // 0's K / V / table rows follow the rows' positions, and the queries'
+    // rows follow those, so the prologue waits on about two round trips.
+    const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
+    Meta<D, WAVES> m1, m2;
+    Data<D, WAVES> dnext;
+    if (ntiles > 0) {
+        meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end, tid);
+        meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
+    }
+    const FbPre fb = fb_preload<GG::NT>(bt, pis, key_begin, key_end, tid);
+
     // ---- this lane's query columns: load, rotate at q_pos, keep as B operands
     u32x4 qop[QG][GG::NC];
     int qpos[QG], qt[QG], qh[QG];
@@ -433,6 +475,14 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
             my_min = min(my_min, pos);
             my_max = max(my_max, pos);
         }
+    }
+    if (ntiles > 0) {
+        data_load<D, WAVES>(p, dnext, m1, g, key_begin, key_end, tid, kV);
+        cs_load<D, WAVES, ROT>(p, dnext, tid);
+    }
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+        const int pos = qpos[qg];
 #pragma unroll
         for (int c = 0; c < GG::NC; ++c) qop[qg][c] = u32x4{0, 0, 0, 0};
         if (pos >= 0) {
@@ -485,20 +535,11 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     __syncthreads();
     atomicMin(&s_minpos, my_min);
     if constexpr (SKIP) atomicMax(&s_maxpos, my_max);
-    const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
     // Staging pipeline: the data of tile t+2 (and the block ids of t+3) are
     // requested next to the QK of tile t+1, about a tile before they are
     // rotated and stored; indices past the range are clamped and such keys
     // read the zero page, so the requests need no branch.  Tiles 0 and 1 are
     // requested before it is known which tiles the rows need.
-    Meta<D, WAVES> m1, m2;
-    Data<D, WAVES> dnext;
-    if (ntiles > 0) {
-        meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end, tid);
-        meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
-        data_load<D, WAVES>(p, dnext, m1, g, key_begin, key_end, tid, kV);
-        cs_load<D, WAVES, ROT>(p, dnext, tid);
-    }
     __syncthreads();
     const int min_pos = s_minpos;
     // Tiles with no key that any row sees are skipped (not in mass mode, which
@@ -509,9 +550,9 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     // every row (pi and block ids are small and L2-resident): tiles before it
     // need no mask.
     {
-        const int bad = SKIP ? first_bad_key<GG::NT>(p, bt, pis, key_begin, key_end, min_pos, tid, s_maxpos,
+        const int bad = SKIP ? first_bad_key<GG::NT>(p, bt, pis, fb, key_begin, key_end, min_pos, tid, s_maxpos,
                                                      skip ? s_need : nullptr)
-                             : first_bad_key<GG::NT>(p, bt, pis, key_begin, key_end, min_pos, tid);
+                             : first_bad_key<GG::NT>(p, bt, pis, fb, key_begin, key_end, min_pos, tid);
         if (bad != 0x7fffffff) atomicMin(&s_firstbad, bad);
     }
     __syncthreads();
@@ -891,18 +932,59 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
     }
     const int row0 = rb * BM + wave * 16 * QG;   // first row of this wave
 
+    // ---- requests that need nothing from the rows first (as in fwd_kernel)
+    const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
+    Meta<D, WAVES> m1, m2;
+    Data<D, WAVES> dnext;
+    if (ntiles > 0) {
+        meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end, tid);
+        meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
+    }
+    const FbPre fb = fb_preload<GG::NT>(bt, pis, key_begin, key_end, tid);
+
     // ---- A operands: query row lc of each row tile, rotated at its q_pos
     u32x4 qop[QG][GG::NC];
+    int qpos[QG], qtk[QG], qhd[QG];
     int my_min = 0x7fffffff;
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
         const int row = row0 + 16 * qg + lc;
         const bool valid = row < nrows;
-        const int qt = q0 + (valid ? row / p.group : 0);
-        const int qh = g * p.group + (valid ? row % p.group : 0);
-        int pos = valid ? p.q_pos[qt] : -1;
+        qtk[qg] = q0 + (valid ? row / p.group : 0);
+        qhd[qg] = g * p.group + (valid ? row % p.group : 0);
+        int pos = valid ? p.q_pos[qtk[qg]] : -1;
         if (pos >= p.max_pos) pos = -1;
         if (valid) my_min = min(my_min, pos);
+        qpos[qg] = pos;
+    }
+    // ---- the rows this lane's scores belong to: 4*lg + i of each row tile.
+    // Rows past the end read the first row's LSE (in range); the value is
+    // not used.
+    float lse2[QG][4];
+    int rpos[QG][4];
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = row0 + 16 * qg + 4 * lg + i;
+            const bool valid = row < nrows;
+            const int qt = q0 + (valid ? row / p.group : 0);
+            const int qh = g * p.group + (valid ? row % p.group : 0);
+            int pos = valid ? p.q_pos[qt] : -1;
+            const float ls = p.lse_in[(size_t)qt * p.hq + qh];
+            if (pos >= p.max_pos) pos = -1;
+            rpos[qg][i] = pos;
+            // invalid rows, and rows with nothing visible (-inf) or NaN,
+            // contribute exp2(-inf) = 0
+            lse2[qg][i] = pos >= 0 && ls > -INFINITY ? ls * 1.4426950408889634f : INFINITY;
+        }
+    if (ntiles > 0) {
+        data_load<D, WAVES>(p, dnext, m1, g, key_begin, key_end, tid, false);
+        cs_load<D, WAVES, ROT>(p, dnext, tid);
+    }
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+        const int pos = qpos[qg], qt = qtk[qg], qh = qhd[qg];
 #pragma unroll
         for (int c = 0; c < GG::NC; ++c) qop[qg][c] = u32x4{0, 0, 0, 0};
         if (pos >= 0) {
@@ -921,46 +1003,15 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
             }
         }
     }
-    // ---- the rows this lane's scores belong to: 4*lg + i of each row tile
-    float lse2[QG][4];
-    int rpos[QG][4];
-#pragma unroll
-    for (int qg = 0; qg < QG; ++qg)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = row0 + 16 * qg + 4 * lg + i;
-            const bool valid = row < nrows;
-            const int qt = q0 + (valid ? row / p.group : 0);
-            const int qh = g * p.group + (valid ? row % p.group : 0);
-            int pos = valid ? p.q_pos[qt] : -1;
-            if (pos >= p.max_pos) pos = -1;
-            rpos[qg][i] = pos;
-            float l2 = INFINITY;   // invalid rows contribute exp2(-inf) = 0
-            if (pos >= 0) {
-                const float ls = p.lse_in[(size_t)qt * p.hq + qh];
-                // -inf (nothing visible) or NaN: contribute nothing
-                l2 = (ls > -INFINITY) ? ls * 1.4426950408889634f : INFINITY;
-            }
-            lse2[qg][i] = l2;
-        }
     const u32x4 ones_a = lc == 0 ? u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u} : u32x4{0, 0, 0, 0};
     const float sc = p.scale_log2;
 
     __syncthreads();
     atomicMin(&s_minpos, my_min);
-    const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
-    Meta<D, WAVES> m1, m2;
-    Data<D, WAVES> dnext;
-    if (ntiles > 0) {
-        meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end, tid);
-        meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
-        data_load<D, WAVES>(p, dnext, m1, g, key_begin, key_end, tid, false);
-        cs_load<D, WAVES, ROT>(p, dnext, tid);
-    }
     __syncthreads();
     const int min_pos = s_minpos;
     {
-        const int bad = first_bad_key<GG::NT>(p, bt, pis, key_begin, key_end, min_pos, tid);
+        const int bad = first_bad_key<GG::NT>(p, bt, pis, fb, key_begin, key_end, min_pos, tid);
         if (bad != 0x7fffffff) atomicMin(&s_firstbad, bad);
     }
     __syncthreads();
