@@ -84,9 +84,10 @@ __device__ __forceinline__ void interleave_hint() {
 }
 
 // Rotate 8 RoPE pairs: lo holds x[i..i+7], hi holds x[i+d/2..i+d/2+7] (bf16),
-// c/s the cos/sin of pos * theta^(-2(i+e)/d).  Result rounded to bf16.
+// c/s the cos/sin of pos * theta^(-2(i+e)/d).  Result times scale (fp32),
+// rounded to bf16.
 __device__ __forceinline__ void rope8(u32x4 &lo, u32x4 &hi, const f32x4 c0, const f32x4 c1,
-                                      const f32x4 s0, const f32x4 s1) {
+                                      const f32x4 s0, const f32x4 s1, float scale = 1.f) {
     const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
     const float s[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     u32x4 ro, rh;
@@ -95,8 +96,8 @@ __device__ __forceinline__ void rope8(u32x4 &lo, u32x4 &hi, const f32x4 c0, cons
         const float a0 = bf_lo(lo[e]), a1 = bf_hi(lo[e]);
         const float b0 = bf_lo(hi[e]), b1 = bf_hi(hi[e]);
         const float cc0 = c[2 * e], cc1 = c[2 * e + 1], ss0 = s[2 * e], ss1 = s[2 * e + 1];
-        ro[e] = pack2(fmaf(a0, cc0, -b0 * ss0), fmaf(a1, cc1, -b1 * ss1));
-        rh[e] = pack2(fmaf(a0, ss0, b0 * cc0), fmaf(a1, ss1, b1 * cc1));
+        ro[e] = pack2(fmaf(a0, cc0, -b0 * ss0) * scale, fmaf(a1, cc1, -b1 * ss1) * scale);
+        rh[e] = pack2(fmaf(a0, ss0, b0 * cc0) * scale, fmaf(a1, ss1, b1 * cc1) * scale);
     }
     lo = ro;
     hi = rh;
@@ -959,7 +960,10 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
     }
     // ---- the rows this lane's scores belong to: 4*lg + i of each row tile.
     // Rows past the end read the first row's LSE (in range); the value is
-    // not used.
+    // not used.  Every score accumulator starts at -lse (log2 units) and the
+    // queries carry the scale log2(e)/sqrt(d), so an S tile holds exactly the
+    // exp2 argument s * scale - lse.
+    const float sc = p.scale_log2;
     float lse2[QG][4];
     int rpos[QG][4];
 #pragma unroll
@@ -978,6 +982,9 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
             // contribute exp2(-inf) = 0
             lse2[qg][i] = pos >= 0 && ls > -INFINITY ? ls * 1.4426950408889634f : INFINITY;
         }
+    f32x4 s_init[QG];
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) s_init[qg] = f32x4{-lse2[qg][0], -lse2[qg][1], -lse2[qg][2], -lse2[qg][3]};
     if (ntiles > 0) {
         data_load<D, WAVES>(p, dnext, m1, g, key_begin, key_end, tid, false);
         cs_load<D, WAVES, ROT>(p, dnext, tid);
@@ -997,14 +1004,13 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
                 const float *cr = p.cos_tab + (size_t)pos * GG::HALF + i0;
                 const float *sr = p.sin_tab + (size_t)pos * GG::HALF + i0;
                 rope8(lo, hi, *reinterpret_cast<const f32x4 *>(cr), *reinterpret_cast<const f32x4 *>(cr + 4),
-                      *reinterpret_cast<const f32x4 *>(sr), *reinterpret_cast<const f32x4 *>(sr + 4));
+                      *reinterpret_cast<const f32x4 *>(sr), *reinterpret_cast<const f32x4 *>(sr + 4), sc);
                 qop[qg][c] = lo;
                 qop[qg][c + GG::NC / 2] = hi;
             }
         }
     }
     const u32x4 ones_a = lc == 0 ? u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u} : u32x4{0, 0, 0, 0};
-    const float sc = p.scale_log2;
 
     __syncthreads();
     atomicMin(&s_minpos, my_min);
@@ -1027,7 +1033,7 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
     // 32*kh + 16*T + lc, i.e. key 32*kh + 8*(lc/4) + 4*T + lc%4
     auto qk = [&](const uint16_t *Kb, int kh, f32x4 (&sacc)[QG][2]) {
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) sacc[qg][0] = sacc[qg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qg = 0; qg < QG; ++qg) sacc[qg][0] = sacc[qg][1] = s_init[qg];
 #pragma unroll
         for (int c = 0; c < GG::NC; ++c) {
             const int ch = 4 * c + lg;
@@ -1062,7 +1068,7 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
 #pragma unroll
                         for (int e = 0; e < 2; ++e) {
                             const int i = 2 * h2 + e;
-                            float x = fmaf(sacc[qg][T][i], sc, -lse2[qg][i]);
+                            float x = sacc[qg][T][i];
                             if constexpr (!FULL) x = kp <= rpos[qg][i] ? x : -INFINITY;
                             pr[e] = fast_exp2(x);
                         }
