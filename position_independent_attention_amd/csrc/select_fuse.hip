@@ -104,12 +104,25 @@ __global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
     const int k = p.sel_off[s + 1] - p.sel_off[s];
     int32_t *out = p.sel_idx + p.sel_off[s];
     if (r < 0 || r >= p.batch || k <= 0) return;
-    int kvl = p.kv_len[r];
-    kvl = kvl < 0 ? 0 : (kvl > p.kv_stride ? p.kv_stride : kvl);
-    const int lo = max(st, 0), hi = min(st + max(L, 0), kvl);
     const int32_t *pis = p.kv_pos + (size_t)r * p.kv_stride;
     const float *mass = p.mass + (size_t)r * p.kv_stride;
-    const bool cached = hi - lo <= 256 * kTopkCache;
+    // A span that fits in registers requests its slots (clamped into the
+    // request's row) beside the request's length, not after it.
+    const int lo = max(st, 0), hi_span = min(st + max(L, 0), p.kv_stride);
+    const bool cached = hi_span - lo <= 256 * kTopkCache;
+    int32_t cpi[kTopkCache];
+    uint32_t cms[kTopkCache];
+    if (cached) {
+#pragma unroll
+        for (int u = 0; u < kTopkCache; ++u) {
+            const int jc = min(lo + 256 * u + tid, max(hi_span - 1, 0));   // in the row for any u
+            cpi[u] = pis[jc];
+            cms[u] = __float_as_uint(mass[jc]);
+        }
+    }
+    int kvl = p.kv_len[r];
+    kvl = kvl < 0 ? 0 : (kvl > p.kv_stride ? p.kv_stride : kvl);
+    const int hi = min(hi_span, kvl);
 
     uint32_t ck[kTopkCache];
     bool cc[kTopkCache];
@@ -134,10 +147,9 @@ __global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
 #pragma unroll
         for (int u = 0; u < kTopkCache; ++u) {
             const int j = lo + 256 * u + tid;
-            const int jc = min(j, max(hi - 1, 0));   // in range for any j
-            const bool c = j < hi && pis[jc] >= 0;
+            const bool c = j < hi && cpi[u] >= 0;
             cc[u] = c;
-            ck[u] = c ? __float_as_uint(mass[jc]) : 0u;
+            ck[u] = c ? cms[u] : 0u;
             mine += c;
         }
     } else {
