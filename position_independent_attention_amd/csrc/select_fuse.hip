@@ -216,11 +216,16 @@ __global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
 // One workgroup per (fused block fb, request r), over every kv head: fresh
 // K rows are copied 16 bytes at a time; fresh V rows are staged in LDS with
 // 16-byte loads and written channel-major, 8 slots (16 bytes) per store.
-// Only the fresh slots of a partial last block are written.
+// Only the fresh slots of a partial last block are written.  The kv heads
+// go in passes of up to kFuseHeads, every load of a pass issued before its
+// first store, so a pass waits on one round trip.
+constexpr int kFuseHeads = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void fuse_kernel(FuseParams p) {
     constexpr int CPR = D / 8;   // 16-byte chunks per row
-    __shared__ __attribute__((aligned(16))) uint16_t s_v[kBlock][D + 8];
+    static_assert(kBlock * CPR <= 256, "one row chunk per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t s_v[kFuseHeads][kBlock][D + 8];
     const int fb = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
     const int row0 = max(0, p.sel_req_off[r]);
     const int cnt = min(p.sel_req_off[r + 1], p.n_sel) - row0;
@@ -239,37 +244,43 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseParams p) {
     const int blk = p.block_table[(size_t)r * p.max_blocks + bidx];
     if (blk < 0 || blk >= p.num_blocks) return;
     const int rowb = row0 + kBlock * fb;
+    // this thread's chunk: slot sl, 16-byte column c
+    const int sl = tid / CPR, c = tid % CPR;
+    const bool has = tid < kBlock * CPR;
+    const bool fresh = has && sl < n_here;
 
-    for (int g = 0; g < p.hkv; ++g) {
-        // K rows: token-major in the pool
-        for (int t = tid; t < kBlock * CPR; t += 256) {
-            const int sl = t / CPR, c = t % CPR;
-            if (sl < n_here) {
-                const u32x4 v =
-                    *reinterpret_cast<const u32x4 *>(p.k_new + ((size_t)(rowb + sl) * p.hkv + g) * D + 8 * c);
-                *reinterpret_cast<u32x4 *>(p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + sl) * D + 8 * c) = v;
+    for (int g0 = 0; g0 < p.hkv; g0 += kFuseHeads) {
+        const int ng = min(kFuseHeads, p.hkv - g0);
+        u32x4 kc[kFuseHeads], vc[kFuseHeads];
+#pragma unroll
+        for (int gi = 0; gi < kFuseHeads; ++gi) {
+            kc[gi] = vc[gi] = u32x4{0u, 0u, 0u, 0u};
+            if (gi < ng && fresh) {
+                const size_t src = ((size_t)(rowb + sl) * p.hkv + g0 + gi) * D + 8 * c;
+                kc[gi] = *reinterpret_cast<const u32x4 *>(p.k_new + src);
+                vc[gi] = *reinterpret_cast<const u32x4 *>(p.v_new + src);
             }
         }
-        // V rows: stage token-major ...
-        for (int t = tid; t < kBlock * CPR; t += 256) {
-            const int sl = t / CPR, c = t % CPR;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (sl < n_here) v = *reinterpret_cast<const u32x4 *>(p.v_new + ((size_t)(rowb + sl) * p.hkv + g) * D + 8 * c);
-            *reinterpret_cast<u32x4 *>(&s_v[sl][8 * c]) = v;
+#pragma unroll
+        for (int gi = 0; gi < kFuseHeads; ++gi) {
+            if (gi < ng && fresh)   // K rows: token-major in the pool
+                *reinterpret_cast<u32x4 *>(p.k_pool + (((size_t)blk * p.hkv + g0 + gi) * kBlock + sl) * D + 8 * c) =
+                    kc[gi];
+            if (gi < ng && has) *reinterpret_cast<u32x4 *>(&s_v[gi][sl][8 * c]) = vc[gi];
         }
         __syncthreads();
-        // ... and write channel-major: thread -> (channel d, slots 8h .. 8h+7)
-        for (int t = tid; t < 2 * D; t += 256) {
-            const int d = t >> 1, h = t & 1;
-            uint16_t *dst = p.v_pool + (((size_t)blk * p.hkv + g) * D + d) * kBlock + 8 * h;
+        // V: channel-major, thread -> (head, channel d, slots 8h .. 8h+7)
+        for (int t = tid; t < ng * 2 * D; t += 256) {
+            const int gi = t / (2 * D), d = (t >> 1) % D, h = t & 1;
+            uint16_t *dst = p.v_pool + (((size_t)blk * p.hkv + g0 + gi) * D + d) * kBlock + 8 * h;
             if (8 * h + 8 <= n_here) {
                 u32x4 w;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    w[e] = (uint32_t)s_v[8 * h + 2 * e][d] | ((uint32_t)s_v[8 * h + 2 * e + 1][d] << 16);
+                    w[e] = (uint32_t)s_v[gi][8 * h + 2 * e][d] | ((uint32_t)s_v[gi][8 * h + 2 * e + 1][d] << 16);
                 *reinterpret_cast<u32x4 *>(dst) = w;
             } else {
-                for (int i = 0; i < 8 && 8 * h + i < n_here; ++i) dst[i] = s_v[8 * h + i][d];
+                for (int i = 0; i < 8 && 8 * h + i < n_here; ++i) dst[i] = s_v[gi][8 * h + i][d];
             }
         }
         __syncthreads();
