@@ -53,7 +53,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attended KV tokens/s + % of HBM/MFMA roofline (GQA 32q/8kv, d=128)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
-TRAFFIC_KERNEL = "fwd_kernel<128, 2, 8, 0, false>"
+TRAFFIC_KERNEL = "fwd_kernel<128, 2, 8, 0, false, true>"
 # the files whose change invalidates a traffic measurement of that kernel
 TRAFFIC_SOURCES = ["position_independent_attention_amd/csrc/attn_fwd.hip",
                    "position_independent_attention_amd/csrc/pic_internal.h",
@@ -314,7 +314,7 @@ def main():
     pairs = visible_pairs(w)
     flops = pairs * w.num_q_heads * 4 * w.head_dim
     achieved = flops / (op_ms["prefill"] / 1e3) / 1e12
-    roofline = {"kernel": "pic_attn_prefill, step 1: fwd_kernel<128, 2, 8, 0, false> (split partials) + merge_kernel; "
+    roofline = {"kernel": "pic_attn_prefill, step 1: fwd_kernel<128, 2, 8, 0, false, true> (split partials) + merge_kernel; "
                           "the duration is the whole call's",
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
