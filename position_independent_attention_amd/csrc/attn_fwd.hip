@@ -31,9 +31,9 @@
 //     each key's pi (every key rotated once per workgroup however many rows
 //     read it), rounded to bf16 and written to the other LDS buffer with the
 //     V^T tile (a plain copy: V is stored head-dim-major per block);
-//   - the barrier also ANDs a per-thread "every key of the next tile is
-//     usable and visible to every row of the workgroup" flag, which selects a
-//     mask-free fast path.
+//   - a pre-pass over the workgroup's key range finds the first key that is
+//     unusable or not visible to every row; tiles before it take a mask-free
+//     fast path.
 //   Softmax uses a lazy rescale: the running column max only moves (and O is
 //   rescaled) when a tile's max exceeds it by more than 2^8, so exp2 of
 //   (score*scale - max) stays below 256 and the O accumulator is almost never
@@ -602,12 +602,11 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     //   R3  PV(half 1)            || rotate + stage the next tile
     //   --  barrier
     //   R4  QK(next tile, half 0)
-    // Every softmax uses the running max as it stood after the previous half
-    // (so the scores and the max reduction are independent of the MFMAs in
-    // flight); the O / row-sum rescale, when the max moved by more than 2^8,
-    // happens after that half's PV, outside the interleaved regions.  A half
-    // whose max jumps by more than 2^64 recomputes its P first (never taken
-    // for finite-range data, kept for safety).
+    // Every softmax uses the reference max the accumulators are in (so the
+    // scores and the max reduction are independent of the MFMAs in flight);
+    // when a half's max passes it by more than 2^8 (rare after the first
+    // keys), the reference moves, the accumulators follow before that half's
+    // PV and its P is formed again.
     auto qk_half = [&](const uint16_t *Kb, int kh, f32x4 (&sacc)[QG][2]) {
 #pragma unroll
         for (int qg = 0; qg < QG; ++qg) sacc[qg][0] = sacc[qg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
