@@ -413,7 +413,10 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
 
     const int nwg = p.row_blocks * p.hkv * p.num_splits * p.batch;
     int lid = xcd_remap(blockIdx.x, nwg);
-    const int rb = lid % p.row_blocks;
+    // With tile skipping the row blocks of position-sorted queries see more
+    // keys the later they come: dispatch them last first, so that the
+    // longest workgroups start at once and the short ones fill the tail.
+    const int rb = SKIP ? p.row_blocks - 1 - lid % p.row_blocks : lid % p.row_blocks;
     lid /= p.row_blocks;
     const int g = lid % p.hkv;
     lid /= p.hkv;
