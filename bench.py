@@ -10,7 +10,7 @@ d = 128, theta 5e5):
   3. kv_fuse_scatter    4,928 recomputed K/V rows into request-private blocks
   4. pic_attn_prefill   attention over the fused cache
   5. pic_attn_decode    one generated token over the fused cache
-(plus two small device copies that restore the un-fused pi / kv_len so that
+(plus one small device copy that restores the un-fused pi / kv_len so that
 every step starts from the same cache).
 
 The step is captured once as a HIP graph and replayed once per timed step
@@ -208,8 +208,14 @@ def main():
     dc = pic.to_device(w, dev, sel_off=sel_off)
     kv0 = dc.max_kv_len
     kv_fused = ((kv0 + 15) // 16) * 16 + nsel
-    kv_pos0 = dc.kv_pos.clone()
-    kv_len0 = dc.kv_len.clone()
+    # pi and kv_len live in one buffer, so that one copy restores the un-fused
+    # cache before every step
+    npos = dc.kv_pos.numel()
+    state0 = torch.cat([dc.kv_pos.reshape(-1), dc.kv_len.reshape(-1)])
+    state = state0.clone()
+    dc.kv_pos = state[:npos].view(dc.kv_pos.shape)
+    dc.kv_len = state[npos:]
+    kv_pos0 = state0[:npos].view(dc.kv_pos.shape)
 
     def t(a):
         a = np.ascontiguousarray(a)
@@ -238,8 +244,7 @@ def main():
 
     def step(evs=None, st=None):
         st = stream if st is None else st
-        dc.kv_pos.copy_(kv_pos0)
-        dc.kv_len.copy_(kv_len0)
+        state.copy_(state0)
         dc.max_kv_len = kv0
         if evs: evs[0].record(st)
         pic.pic_attn_prefill(ctx, dc, out1, lse1, ws=ws, stream=st)
@@ -350,8 +355,7 @@ def main():
         # prefill call with keys_prerotated = 1, i.e. the keys used as stored.  It
         # runs on the same pool bytes: the kernels' work does not depend on the
         # key values.
-        dc.kv_pos.copy_(kv_pos0)
-        dc.kv_len.copy_(kv_len0)
+        state.copy_(state0)
         dc.max_kv_len = kv0
         ctx_pr = pic.Context(w.num_q_heads, w.num_kv_heads, w.head_dim, w.rope_theta, w.max_position,
                              keys_prerotated=True)
@@ -405,8 +409,7 @@ def main():
     if not args.no_anchor:
         # Anchor extraction: per-span top 5% of slots by stored-key norm over the
         # un-fused long-context cache (reads K once: HBM-bound).
-        dc.kv_pos.copy_(kv_pos0)
-        dc.kv_len.copy_(kv_len0)
+        state.copy_(state0)
         dc.max_kv_len = kv0
         a_off = pic.pic_select_offsets(w.span_len, ANCHOR_RATIO)
         na = int(a_off[-1])
