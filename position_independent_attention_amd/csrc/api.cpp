@@ -115,13 +115,11 @@ DecodePlan plan_decode(int batch, int hkv, int max_kv_len) {
     len = std::max(512LL, std::min(len, ((long long)max_kv_len + 127) / 128 * 128));
     // Two workgroups per CU are resident at once.  A plan that overflows one
     // such round by less than a whole round would leave its second round
-    // mostly idle: take splits long enough for one workgroup per CU instead
-    // (measured: 4% faster than one round of two per CU, which spends more
-    // of each wave's short range filling and draining its prefetch).
+    // mostly idle: take one round of longer splits instead.
     const long long resident = 2LL * kCUs;
     const long long nwg = rows * ((max_kv_len + len - 1) / len);
     if (nwg > resident && nwg < 2 * resident) {
-        const long long per_row = std::max(1LL, (long long)kCUs / rows);
+        const long long per_row = std::max(1LL, resident / rows);
         len = ((max_kv_len + per_row - 1) / per_row + 127) / 128 * 128;
         len = std::max(512LL, len);
     }
