@@ -1,9 +1,9 @@
 """HIP path vs the CPU oracle, element by element, through the C ABI.
 
-Bar: bf16 outputs max abs <= 2e-2 and mean abs <= 2e-3 (plus rel-L2 <= 1e-2);
-LSE abs <= 1e-3; selection mass abs <= 5e-4; selected sets identical outside
-a 1e-3 band around each span's k-th mass (ties to the lower index); fusion
-bit-exact.  Small shapes compare every output; the full-size shapes compare
+Bar (tests/util.py): bf16 outputs max abs <= 2e-2 and mean abs <= 2e-3 (plus
+rel-L2 <= 1e-2); LSE abs <= 1e-2; selection mass within 2% + 1e-5; selected
+sets identical outside a 1e-3 band around each span's k-th mass (ties to the
+lower index); fusion bit-exact.  Small shapes compare every output; the full-size shapes compare
 sampled rows and size-independent properties.
 """
 import dataclasses
