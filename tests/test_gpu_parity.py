@@ -290,6 +290,9 @@ def small_select_workloads():
         # d = 64 with 160 rows per kv head: the 4-row-tile mass pass at d = 64
         "d64_many_rows": lambda: W.custom(115, Hq=8, Hkv=2, d=64, theta=1e4, span_lens=[[300, 200], [150]],
                                           q_len=[40, 33], ratio=0.2),
+        # 16 kv heads (MHA): the fusion copies its heads in two passes of 8
+        "mha16": lambda: W.custom(119, Hq=16, Hkv=16, d=128, theta=5e5, span_lens=[[200, 77], [90]],
+                                  q_len=[9, 20], ratio=0.3),
     }
 
 
@@ -363,7 +366,7 @@ def test_select_full_size_properties():
 
 # ---------------------------------------------------------------- fusion
 
-@pytest.mark.parametrize("name", ["tiny", "shared_small", "edge_spans"])
+@pytest.mark.parametrize("name", ["tiny", "shared_small", "edge_spans", "mha16"])
 def test_fuse_bit_exact_and_second_pass(name):
     """The oracle's own selection is fused by both sides: pool bytes, pi and
     kv_len must match bit for bit, shared blocks stay untouched, and attention
