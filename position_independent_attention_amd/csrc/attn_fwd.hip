@@ -31,9 +31,13 @@
 //     each key's pi (every key rotated once per workgroup however many rows
 //     read it), rounded to bf16 and written to the other LDS buffer with the
 //     V^T tile (a plain copy: V is stored head-dim-major per block);
-//   - a pre-pass over the workgroup's key range finds the first key that is
-//     unusable or not visible to every row; tiles before it take a mask-free
-//     fast path.
+//   - unusable keys (pi = -1, no block, past the end) are cut without a
+//     per-score test: their K rows load as zeros and the QK^T accumulators
+//     start at each key's bias (0, or -inf for an unusable key);
+//   - a pre-pass over the workgroup's key range finds the first and the last
+//     usable key that some row does not see yet; tiles outside that range
+//     take a mask-free fast path (in attention; the mass kernel's pre-pass
+//     also counts unusable keys as needing the mask).
 //   Softmax uses a lazy rescale: the running column max only moves (and O is
 //   rescaled) when a tile's max exceeds it by more than 2^8, so exp2 of
 //   (score*scale - max) stays below 256 and the O accumulator is almost never
@@ -189,6 +193,11 @@ __device__ __forceinline__ int task_key0(int wave, int u) {   // first key of (w
 // Block ids / positions of one tile for this thread's staging tasks, as
 // loaded (at clamped indices); the range check is applied where they are used,
 // one tile later, so that no wait for these loads sits at the tile start.
+// Word 3 of a raw buffer resource on this architecture: 32-bit data format
+// (with a zero format every load would return 0), no swizzle or index stride.
+// A raw load whose byte offset lies past the resource's size returns zeros.
+constexpr int kRsrcWord3 = 0x00020000;
+
 template <int D, int WAVES>
 struct Meta {
     int32_t kblk[Geo<D, WAVES>::KTASK];   // wave-uniform
@@ -230,7 +239,10 @@ __device__ __forceinline__ void meta_load(Meta<D, WAVES> &m, const int32_t *bt, 
     m.vkey_pi = pis[(uint32_t)(bv * 16 + (lane & 15))];
 }
 
-template <int D, int WAVES>
+// ZERO: the K rows of unusable keys are read as zeros (their offsets fall
+// outside the range of the block's buffer resource, and such loads return 0),
+// so that whatever those pool rows hold cannot turn a score into NaN.
+template <int D, int WAVES, bool ZERO = false>
 __device__ __forceinline__ void data_load(const FwdParams &p, Data<D, WAVES> &dt, const Meta<D, WAVES> &m, int g,
                                           int tile, int key_end, int tid, bool need_v) {
     using GG = Geo<D, WAVES>;
@@ -248,8 +260,17 @@ __device__ __forceinline__ void data_load(const FwdParams &p, Data<D, WAVES> &dt
         // block are masked (scores) and zeroed (V) downstream
         const uint16_t *kbase = bok ? p.k_pool + ((size_t)blk * p.hkv + g) * (kBlock * D) : p.zero_page;
         const uint32_t off = (uint32_t)(row * D + 8 * pc);
-        dt.klo[u] = *reinterpret_cast<const u32x4 *>(kbase + off);
-        dt.khi[u] = *reinterpret_cast<const u32x4 *>(kbase + off + GG::HALF);
+        if constexpr (ZERO) {
+            constexpr int kBytes = kBlock * D * 2;   // one (block, kv head) of K
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(kbase), (short)0, kBytes, kRsrcWord3);
+            const int bo = ok ? (int)(2 * off) : 2 * kBytes;
+            dt.klo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, bo, 0, 0));
+            dt.khi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, bo + GG::HALF * 2, 0, 0));
+        } else {
+            dt.klo[u] = *reinterpret_cast<const u32x4 *>(kbase + off);
+            dt.khi[u] = *reinterpret_cast<const u32x4 *>(kbase + off + GG::HALF);
+        }
     }
     if (!need_v) return;
     int half, dd;
@@ -310,26 +331,34 @@ __device__ __forceinline__ FbPre fb_preload(const int32_t *bt, const int32_t *pi
     return f;
 }
 
-// First key of [key_begin, key_end) that is unusable or not visible to the
-// row with the smallest position (INT_MAX if none).  Four keys per thread and
-// step with no early exit, so the loads of all steps can be in flight at once.
+// First key of [key_begin, key_end) that needs the per-score mask (INT_MAX
+// if none), and with last_bad the last such key (-1 if none).  With KEYBIAS
+// only a usable key that the row with the smallest position does not see
+// needs it (unusable keys are then cut by their score bias); otherwise also
+// every unusable key.  Four keys per thread and step with no early exit, so
+// the loads of all steps can be in flight at once.
 // key_begin is a multiple of 64 and kv_stride of 16, so each 4-key load is
 // aligned and stays inside the request's position row.  With s_need, also
 // sets bit t of s_need for every 64-key tile t holding a usable key that the
 // row with the largest position (max_row) sees.
 // The first two steps use the rows preloaded by fb_preload.
-template <int NT>
+template <int NT, bool KEYBIAS>
 __device__ __forceinline__ int first_bad_key(const FwdParams &p, const int32_t *bt, const int32_t *pis,
                                              const FbPre &pre, int key_begin, int key_end, int min_pos, int tid,
-                                             int max_row = -1, uint32_t *s_need = nullptr) {
-    int bad = 0x7fffffff;
+                                             int *last_bad = nullptr, int max_row = -1,
+                                             uint32_t *s_need = nullptr) {
+    int bad = 0x7fffffff, last = -1;
     auto step = [&](int j0, const i32x4 pi, int blk) {
         const bool bok = blk >= 0 && blk < p.num_blocks;
         bool need = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool usable = j0 + i < key_end && bok && pi[i] >= 0 && pi[i] < p.max_pos;
-            if (j0 + i < key_end && !(usable && pi[i] <= min_pos)) bad = min(bad, j0 + i);
+            const bool b = KEYBIAS ? usable && pi[i] > min_pos : j0 + i < key_end && !(usable && pi[i] <= min_pos);
+            if (b) {
+                bad = min(bad, j0 + i);
+                last = max(last, j0 + i);
+            }
             need = need || (usable && pi[i] <= max_row);
         }
         if (s_need && need) {
@@ -345,14 +374,18 @@ __device__ __forceinline__ int first_bad_key(const FwdParams &p, const int32_t *
 #pragma unroll 4
     for (int j0 = key_begin + 4 * tid + 8 * NT; j0 < key_end; j0 += 4 * NT)
         step(j0, *reinterpret_cast<const i32x4 *>(pis + j0), bt[j0 >> 4]);
+    if (last_bad) *last_bad = last;
     return bad;
 }
 
-// Rotate and write one tile into an LDS buffer.  Returns whether every key
-// this thread staged is usable and visible to the workgroup's earliest row.
+// Rotate and write one tile into an LDS buffer.  With s_bias, also writes
+// each key's score bias (0 if usable, -inf if not); with K rows of unusable
+// keys loaded as zeros their scores are then exactly -inf without a
+// per-score test.  Returns whether every key this thread staged is usable
+// and visible to the workgroup's earliest row.
 template <int D, int WAVES, bool ROT>
 __device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uint16_t *Vs, int32_t *s_pi, int tid,
-                                           bool need_v, int min_pos) {
+                                           bool need_v, int min_pos, float *s_bias = nullptr) {
     using GG = Geo<D, WAVES>;
     bool full = true;
 #pragma unroll
@@ -367,6 +400,7 @@ __device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uin
         *reinterpret_cast<u32x4 *>(Ks + koff<D>(kr, GG::PC + pc)) = hi;
         // masked-path visibility is one compare: unusable keys get INT_MAX
         if (pc == 0) s_pi[kk] = pi >= 0 ? pi : 0x7fffffff;
+        if (s_bias && pc == 0) s_bias[kk] = pi >= 0 ? 0.f : -INFINITY;
         full = full && pi >= 0 && pi <= min_pos;
     }
     if (need_v) {
@@ -406,8 +440,10 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * GG::KBUF];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[kV ? 2 * GG::VBUF : 8];
     __shared__ __attribute__((aligned(16))) int32_t s_pi[2 * kTileN];
+    // score bias of each staged key: 0, or -inf for an unusable key
+    __shared__ __attribute__((aligned(16))) float s_bias[2 * kTileN];
     __shared__ float s_red[MODE == kMass ? 2 * WAVES * kTileN : 1];
-    __shared__ int32_t s_minpos, s_firstbad, s_maxpos;
+    __shared__ int32_t s_minpos, s_firstbad, s_lastbad, s_maxpos;
     // bit t: tile t holds a key that some row of the workgroup sees
     __shared__ uint32_t s_need[SKIP ? kNeedWords : 1];
 
@@ -442,6 +478,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     if (tid == 0) {
         s_minpos = 0x7fffffff;
         s_firstbad = 0x7fffffff;
+        s_lastbad = -1;
         s_maxpos = -1;
     }
     if constexpr (SKIP)
@@ -465,13 +502,18 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     int qpos[QG], qt[QG], qh[QG];
     bool qvalid[QG];
     int my_min = 0x7fffffff, my_max = -1;
+    // query token and head of this lane's column in row tile qg (recomputed
+    // for the epilogue rather than kept live through the tile loop)
+    auto row_of = [&](int qg, int &t, int &h) -> bool {
+        const int row = rb * BM + wave * 16 * QG + 16 * qg + lc;
+        const bool v = row < nrows;
+        t = q0 + (v ? row / p.group : 0);
+        h = g * p.group + (v ? row % p.group : 0);
+        return v;
+    };
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
-        const int row = rb * BM + wave * 16 * QG + 16 * qg + lc;
-        qvalid[qg] = row < nrows;
-        const int tl = qvalid[qg] ? row / p.group : 0;
-        qt[qg] = q0 + tl;
-        qh[qg] = g * p.group + (qvalid[qg] ? row % p.group : 0);
+        qvalid[qg] = row_of(qg, qt[qg], qh[qg]);
         int pos = qvalid[qg] ? p.q_pos[qt[qg]] : -1;
         if (pos >= p.max_pos) pos = -1;
         qpos[qg] = pos;
@@ -481,7 +523,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         }
     }
     if (ntiles > 0) {
-        data_load<D, WAVES>(p, dnext, m1, g, key_begin, key_end, tid, kV);
+        data_load<D, WAVES, true>(p, dnext, m1, g, key_begin, key_end, tid, kV);
         cs_load<D, WAVES, ROT>(p, dnext, tid);
     }
 #pragma unroll
@@ -550,17 +592,21 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     // writes every key's partial sum); so is every tile when too many for the
     // bit mask.
     const bool skip = SKIP && MODE != kMass && ntiles <= kNeedWords * 32;
-    // First key of this workgroup's range that is unusable or not visible to
-    // every row (pi and block ids are small and L2-resident): tiles before it
-    // need no mask.
+    // First and last key of this workgroup's range that some row does not see
+    // although it is usable (pi and block ids are small and L2-resident):
+    // tiles outside that range need no per-score mask.
     {
-        const int bad = SKIP ? first_bad_key<GG::NT>(p, bt, pis, fb, key_begin, key_end, min_pos, tid, s_maxpos,
-                                                     skip ? s_need : nullptr)
-                             : first_bad_key<GG::NT>(p, bt, pis, fb, key_begin, key_end, min_pos, tid);
-        if (bad != 0x7fffffff) atomicMin(&s_firstbad, bad);
+        int last = -1;
+        const int bad = SKIP ? first_bad_key<GG::NT, true>(p, bt, pis, fb, key_begin, key_end, min_pos, tid, &last,
+                                                           s_maxpos, skip ? s_need : nullptr)
+                             : first_bad_key<GG::NT, true>(p, bt, pis, fb, key_begin, key_end, min_pos, tid, &last);
+        if (bad != 0x7fffffff) {
+            atomicMin(&s_firstbad, bad);
+            atomicMax(&s_lastbad, last);
+        }
     }
     __syncthreads();
-    const int first_bad = s_firstbad;
+    const int first_bad = s_firstbad, last_bad = s_lastbad;
     // Whether the rows need every tile (the usual case): then the tile order
     // is plain, with no look-up in the mask.  Each wave checks the whole mask.
     bool every = !skip;
@@ -587,11 +633,11 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         // the rows skip tile 0 or 1: request the first two tiles they need
         meta_load<D, WAVES>(m1, bt, pis, key_begin + it0 * kTileN, key_end, tid);
         meta_load<D, WAVES>(m2, bt, pis, key_begin + it1 * kTileN, key_end, tid);
-        data_load<D, WAVES>(p, dnext, m1, g, key_begin + it0 * kTileN, key_end, tid, kV);
+        data_load<D, WAVES, true>(p, dnext, m1, g, key_begin + it0 * kTileN, key_end, tid, kV);
         cs_load<D, WAVES, ROT>(p, dnext, tid);
     }
     if (SKIP ? it0 < ntiles : ntiles > 0) {
-        (void)data_store<D, WAVES, ROT>(dnext, Ks, Vs, s_pi, tid, kV, min_pos);
+        (void)data_store<D, WAVES, ROT>(dnext, Ks, Vs, s_pi, tid, kV, min_pos, s_bias);
         __syncthreads();
     }
     const float sc = p.scale_log2;
@@ -610,9 +656,14 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     // when a half's max passes it by more than 2^8 (rare after the first
     // keys), the reference moves, the accumulators follow before that half's
     // PV and its P is formed again.
-    auto qk_half = [&](const uint16_t *Kb, int kh, f32x4 (&sacc)[QG][2]) {
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) sacc[qg][0] = sacc[qg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // buf: LDS buffer of the tile.  The accumulators start at the keys'
+    // score bias (-inf cuts an unusable key; its K row is zero).
+    auto qk_half = [&](int buf, int kh, f32x4 (&sacc)[QG][2]) {
+        const uint16_t *Kb = Ks + buf * GG::KBUF;
+        // sacc[.][T][i] holds key 32 kh + 8 lg + 4 T + i
+        const float *bb = s_bias + buf * kTileN + 32 * kh + 8 * lg;
+        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bb);
+        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(bb + 4);
         // d-chunk outermost: 2*QG independent accumulators separate the
         // dependent MFMAs of one accumulator chain
         // rows 32*kh + 16*T + lc (T = 0, 1), chunk 4c + lg: the XOR stays
@@ -625,8 +676,8 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
             const u32x4 a1 = *reinterpret_cast<const u32x4 *>(k0 + 16 * 8);
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) {
-                sacc[qg][0] = mfma16(a0, qop[qg][c], sacc[qg][0]);
-                sacc[qg][1] = mfma16(a1, qop[qg][c], sacc[qg][1]);
+                sacc[qg][0] = mfma16(a0, qop[qg][c], c == 0 ? b0 : sacc[qg][0]);
+                sacc[qg][1] = mfma16(a1, qop[qg][c], c == 0 ? b1 : sacc[qg][1]);
             }
         }
     };
@@ -722,20 +773,20 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
 
     f32x4 sA[QG][2], sB[QG][2];
     if (SKIP ? it0 < ntiles : ntiles > 0) {
-        qk_half(Ks, 0, sA);
-        data_load<D, WAVES>(p, dnext, m2, g, key_begin + it1 * kTileN, key_end, tid, kV);
+        qk_half(0, 0, sA);
+        data_load<D, WAVES, true>(p, dnext, m2, g, key_begin + it1 * kTileN, key_end, tid, kV);
         meta_load<D, WAVES>(m2, bt, pis, key_begin + it2 * kTileN, key_end, tid);
     }
 
     // One tile: the k-th processed, tile index it; n1, n2, n3 the next three
-    // needed tiles.  MORE: n1 exists (stage it), FULL: no masking needed.
+    // needed tiles.  MORE: n1 exists (stage it), FULL: no per-score mask
+    // (every usable key is visible to every row).
     // Each region is straight-line code so the MFMA / VALU interleave hints
     // apply to it.
     auto tile_body = [&](auto more_c, auto full_c, int k, int it, int n1, int n2, int n3) {
         constexpr bool MORE = decltype(more_c)::value;
         const int cur = (SKIP ? k : it) & 1;
         const int tile = key_begin + it * kTileN;
-        const uint16_t *Kc = Ks + cur * GG::KBUF;
         const uint16_t *Vc = Vs + (kV ? cur * GG::VBUF : 0);
         const int32_t *pc_ = s_pi + cur * kTileN;
         u32x4 pb0[QG], pb1[QG];
@@ -745,7 +796,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         for (int u = 0; u < 16; ++u) cs[u] = 0.f;
 
         // R1: QK(half 1) || softmax(half 0)
-        qk_half(Kc, 1, sB);
+        qk_half(cur, 1, sB);
         softmax_half(full_c, sA, pc_, 0, pb0, mx0, cs);
         interleave_hint<2 * QG * GG::NC, 4>();
         if constexpr (MODE != kMass) settle(full_c, sA, pc_, 0, pb0, mx0, cs);
@@ -780,7 +831,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         bool f = true;
         if constexpr (MORE)
             f = data_store<D, WAVES, ROT>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs + (kV ? (cur ^ 1) * GG::VBUF : 0),
-                                     s_pi + (cur ^ 1) * kTileN, tid, kV, min_pos);
+                                     s_pi + (cur ^ 1) * kTileN, tid, kV, min_pos, s_bias + (cur ^ 1) * kTileN);
         if constexpr (MODE != kMass) interleave_hint<QG * (D / 16 + 1), 3>();
         (void)f;
         __syncthreads();
@@ -798,8 +849,8 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         }
         // R4: QK(next tile, half 0) || request the tile after it
         if constexpr (MORE) {
-            qk_half(Ks + (cur ^ 1) * GG::KBUF, 0, sA);
-            data_load<D, WAVES>(p, dnext, m2, g, SKIP ? key_begin + n2 * kTileN : tile + 2 * kTileN, key_end, tid,
+            qk_half(cur ^ 1, 0, sA);
+            data_load<D, WAVES, true>(p, dnext, m2, g, SKIP ? key_begin + n2 * kTileN : tile + 2 * kTileN, key_end, tid,
                                 kV);
             meta_load<D, WAVES>(m2, bt, pis, SKIP ? key_begin + n3 * kTileN : tile + 3 * kTileN, key_end, tid);
         }
@@ -807,38 +858,45 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
-    // Tiles before the one holding the first unusable / not-yet-visible key
-    // run mask-free, the rest masked; each loop keeps its own register
-    // allocation.  A partial last tile is always masked.
-    const int t_split = first_bad == 0x7fffffff ? ntiles : (first_bad - key_begin) / kTileN;
-    const bool last_partial = ntiles > 0 && key_end - (key_begin + (ntiles - 1) * kTileN) < kTileN;
+    // Tiles [t1, t2) hold the usable keys some row does not see and run
+    // masked; the rest run mask-free (before that range: the shared context,
+    // after it: rows appended behind the query block, such as fused rows).
+    // Each loop keeps its own register allocation; the outer loops run at
+    // most twice.
+    const int t1 = first_bad == 0x7fffffff ? ntiles : (first_bad - key_begin) / kTileN;
+    const int t2 = last_bad < 0 ? ntiles : (last_bad - key_begin) / kTileN + 1;
+    auto full_tile = [&](int i) { return i < t1 || i >= t2; };
     if constexpr (SKIP) {
         // the needed tiles in order: (it, n1, n2) advance together
         int k = 0, it = it0, n1 = it1, n2 = it2;
-        for (; n1 < ntiles && it < t_split; ++k) {
+        for (; n1 < ntiles && full_tile(it); ++k) {
             const int n3 = next_tile(n2);
             tile_body(T_{}, T_{}, k, it, n1, n2, n3);
             it = n1, n1 = n2, n2 = n3;
         }
-        for (; n1 < ntiles; ++k) {
+        for (; n1 < ntiles && !full_tile(it); ++k) {
             const int n3 = next_tile(n2);
             tile_body(T_{}, F_{}, k, it, n1, n2, n3);
             it = n1, n1 = n2, n2 = n3;
         }
+        for (; n1 < ntiles; ++k) {
+            const int n3 = next_tile(n2);
+            tile_body(T_{}, T_{}, k, it, n1, n2, n3);
+            it = n1, n1 = n2, n2 = n3;
+        }
         if (it < ntiles) {
-            if (it < t_split && !(it == ntiles - 1 && last_partial))
-                tile_body(F_{}, T_{}, k, it, ntiles, ntiles, ntiles);
-            else
-                tile_body(F_{}, F_{}, k, it, ntiles, ntiles, ntiles);
+            if (full_tile(it)) tile_body(F_{}, T_{}, k, it, ntiles, ntiles, ntiles);
+            else tile_body(F_{}, F_{}, k, it, ntiles, ntiles, ntiles);
         }
     } else {
-        const int nf = min(t_split, ntiles - 1);
+        const int nl = ntiles - 1;   // tiles with a successor to stage
         int it = 0;
-        for (; it < nf; ++it) tile_body(T_{}, T_{}, it, it, 0, 0, 0);
-        for (; it < ntiles - 1; ++it) tile_body(T_{}, F_{}, it, it, 0, 0, 0);
+        for (; it < nl && full_tile(it); ++it) tile_body(T_{}, T_{}, it, it, 0, 0, 0);
+        for (; it < nl && !full_tile(it); ++it) tile_body(T_{}, F_{}, it, it, 0, 0, 0);
+        for (; it < nl; ++it) tile_body(T_{}, T_{}, it, it, 0, 0, 0);
         if (ntiles > 0) {
-            if (t_split >= ntiles && !last_partial) tile_body(F_{}, T_{}, ntiles - 1, ntiles - 1, 0, 0, 0);
-            else tile_body(F_{}, F_{}, ntiles - 1, ntiles - 1, 0, 0, 0);
+            if (full_tile(nl)) tile_body(F_{}, T_{}, nl, nl, 0, 0, 0);
+            else tile_body(F_{}, F_{}, nl, nl, 0, 0, 0);
         }
     }
 #pragma unroll
@@ -849,8 +907,9 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
         const float lt = col_sum(acc_l[qg][0]);   // row 0 lives in lane group 0
-        if (!qvalid[qg]) continue;
-        const size_t rowid = (size_t)qt[qg] * p.hq + qh[qg];
+        int t, h;
+        if (!row_of(qg, t, h)) continue;
+        const size_t rowid = (size_t)t * p.hq + h;
         if (p.num_splits == 1) {
             const bool any = lt > 0.f;
             if constexpr (kV) {
@@ -1019,7 +1078,7 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
     __syncthreads();
     const int min_pos = s_minpos;
     {
-        const int bad = first_bad_key<GG::NT>(p, bt, pis, fb, key_begin, key_end, min_pos, tid);
+        const int bad = first_bad_key<GG::NT, false>(p, bt, pis, fb, key_begin, key_end, min_pos, tid);
         if (bad != 0x7fffffff) atomicMin(&s_firstbad, bad);
     }
     __syncthreads();

@@ -53,9 +53,17 @@ def masked_inside_blocks():
     n = int(w.kv_len[0]) - 24
     holes = rng.choice(n, size=60, replace=False)
     w.kv_pos[0, holes] = -1
-    # garbage in a masked slot's V must not leak into the output
+    # garbage in masked slots (NaN in V, NaN and +inf in K) and in the pool
+    # rows past the end of the sequence must not leak into the output
     blk = w.block_table[0, holes[0] // 16]
     w.pool_v[blk, :, :, holes[0] % 16] = 0x7fc0           # bf16 NaN
+    for j, bits in ((holes[1], 0x7fc0), (holes[2], 0x7f80)):  # NaN, +inf
+        w.pool_k[w.block_table[0, j // 16], :, j % 16, :] = bits
+    end = int(w.kv_len[0])
+    assert end % 16, "the last block must be partial"
+    last = w.block_table[0, end // 16]
+    w.pool_k[last, :, end % 16:, :] = 0x7fc0
+    w.pool_v[last, :, :, end % 16:] = 0x7fc0
     return w
 
 
