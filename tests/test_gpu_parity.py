@@ -403,6 +403,35 @@ def test_fuse_bit_exact_and_second_pass(name):
     assert np.max(np.abs(lse2.cpu().numpy() - refl2)) <= LSE_ABS
 
 
+@pytest.mark.parametrize("d,q_len", [(128, 520), (64, 260)])
+def test_fused_pass_with_many_rows_uses_tile_skipping(d, q_len):
+    """Enough query rows for the tile-skipping kernel (8 or more row blocks).
+    Over the fused cache its key range holds stale slots (pi = -1) in the
+    spans, the query block (masked tiles), an alignment pad and the fused rows
+    behind it.  All fused rows are visible to every row, so they run in the
+    mask-free loop after the masked range."""
+    w = W.custom(120 + d, Hq=8, Hkv=2, d=d, theta=5e5, span_lens=[[300, 203, 250]], gaps=[[0, 40, 9]],
+                 q_len=[q_len], ratio=0.25)
+    say(f"fused pass: d={d} q={q_len} kv={w.kv_len.tolist()} rows={q_len * 4}")
+    ctx = H.ctx_for(w)
+    ref_m = oracle.mass(w)
+    ref_off, ref_idx = oracle.select(w, ref_m)
+    req_off = H.req_offsets(w, ref_off)
+    n = int(req_off[-1])
+    pk, pv, kp, kl = oracle.fuse(w, ref_idx, req_off, w.fresh_k[:n], w.fresh_v[:n])
+    assert int(kl[0]) % 16 and int(w.kv_len[0]) % 16, "want a pad and a partial last block"
+    dc = pic.to_device(w, H.DEV)
+    H.fuse(ctx, dc, ref_idx, req_off, w.fresh_k, w.fresh_v)
+    assert np.array_equal(dc.kv_pos.cpu().numpy(), kp)
+    fused = w.copy()
+    fused.pool_k, fused.pool_v, fused.kv_pos, fused.kv_len = pk, pv, kp, kl
+    dc.max_kv_len = int(kl.max())
+    out, lse, _ = H.prefill(ctx, fused, dc)
+    ref_o, ref_l = oracle.attention(fused)
+    compare_out(H.host_bf16(out), ref_o, "O fused")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+
+
 def test_fuse_full_size_with_seeded_selection():
     """Full 32k shape: a seeded selection (15% per span, from the test's own
     generator) fused on both sides; bitwise equal; then sampled rows of the
