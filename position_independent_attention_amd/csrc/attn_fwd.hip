@@ -485,7 +485,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         for (int w = tid; w < kNeedWords; w += GG::NT) s_need[w] = 0u;
 
     // ---- requests that need nothing from the rows go first: block ids and
-    // positions of tiles 0 and 1 and of the first-unusable-key scan.  Tile
+    // positions of tiles 0 and 1 and of the masking pre-pass.  Tile
     // 0's K / V / table rows follow the rows' positions, and the queries'
     // rows follow those, so the prologue waits on about two round trips.
     const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
@@ -828,12 +828,11 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
             const int key = 32 * (lc >> 3) + 8 * lg + 4 * ((lc >> 2) & 1) + (lc & 3);
             s_red[(cur * WAVES + wave) * kTileN + key] = cs[0];
         }
-        bool f = true;
         if constexpr (MORE)
-            f = data_store<D, WAVES, ROT>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs + (kV ? (cur ^ 1) * GG::VBUF : 0),
-                                     s_pi + (cur ^ 1) * kTileN, tid, kV, min_pos, s_bias + (cur ^ 1) * kTileN);
+            (void)data_store<D, WAVES, ROT>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs + (kV ? (cur ^ 1) * GG::VBUF : 0),
+                                            s_pi + (cur ^ 1) * kTileN, tid, kV, min_pos,
+                                            s_bias + (cur ^ 1) * kTileN);
         if constexpr (MODE != kMass) interleave_hint<QG * (D / 16 + 1), 3>();
-        (void)f;
         __syncthreads();
 
         if constexpr (MODE == kMass) {

@@ -372,6 +372,28 @@ def test_select_full_size_properties():
         assert list(sel[sel_off[s]:sel_off[s + 1]]) == sorted(order[:k])
 
 
+@pytest.mark.parametrize("name", ["tiny", "shared_small", "edge_spans", "long_spans", "long_context_full"])
+def test_select_without_mass_output_is_the_same_selection(name):
+    """The mass output is optional: leaving it out must not change the
+    selection by a bit, spans longer than the top-k's register cache
+    included, both with and without the caller's lse."""
+    w = W.long_context() if name == "long_context_full" else small_select_workloads()[name]()
+    ctx = H.ctx_for(w)
+    _, lse, dc = H.prefill(ctx, w)
+    sel_off, _, _ = H.select(ctx, w, dc, lse)
+    nsel = int(sel_off[-1])
+    mass = torch.empty(w.kv_pos.shape, dtype=torch.float32, device=H.DEV)
+    for lse_arg in (lse, None):
+        picks = []
+        for m in (mass, None):
+            got = torch.full((max(nsel, 1),), -7, dtype=torch.int32, device=H.DEV)
+            pic.qc_score_select(ctx, dc, lse_arg, nsel, got, m)
+            torch.cuda.synchronize()
+            picks.append(got.cpu().numpy()[:nsel])
+        assert np.array_equal(picks[0], picks[1]), (name, lse_arg is None)
+        assert not np.any(picks[1] == -7)
+
+
 # ---------------------------------------------------------------- fusion
 
 @pytest.mark.parametrize("name", ["tiny", "shared_small", "edge_spans", "mha16"])
