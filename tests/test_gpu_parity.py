@@ -176,7 +176,7 @@ def test_prefill_full_size_sampled(name):
 
 # ---------------------------------------------------------------- decode
 
-@pytest.mark.parametrize("name", ["small", "small_private", "edge_g8", "d64", "d64_irregular"])
+@pytest.mark.parametrize("name", ["small", "small_private", "edge_g8", "masked_garbage", "d64", "d64_irregular"])
 def test_decode_parity(name):
     if name == "small":
         w = W.decode_heavy(batch=5, n_spans=3, span_tok=80)
@@ -194,6 +194,19 @@ def test_decode_parity(name):
         w = W.custom(109, Hq=16, Hkv=2, d=128, theta=5e5, span_lens=[[2500, 3], [1], [700, 700]],
                      gaps=[[0, 9], [3], [0, 0]], q_len=[1, 1, 1], decode=True)
         w.kv_pos[2, 100:140] = -1
+        if name == "masked_garbage":
+            # NaN / +inf in the masked slots' K and V and past every sequence's
+            # end: none of it may reach the output
+            for j in range(100, 140):
+                blk = w.block_table[2, j // 16]
+                w.pool_k[blk, :, j % 16, :] = 0x7fc0 if j % 2 else 0x7f80
+                w.pool_v[blk, :, :, j % 16] = 0x7fc0
+            for r in range(w.batch):
+                end = int(w.kv_len[r])
+                if end % 16:
+                    last = w.block_table[r, end // 16]
+                    w.pool_k[last, :, end % 16:, :] = 0x7fc0
+                    w.pool_v[last, :, :, end % 16:] = 0x7fc0
     say(f"decode {name}: B={w.batch} kv={w.kv_len.tolist()[:6]}")
     ctx = H.ctx_for(w)
     out, lse, _ = H.decode(ctx, w)
