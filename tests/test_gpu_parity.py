@@ -314,6 +314,8 @@ def small_select_workloads():
         # 16 kv heads (MHA): the fusion copies its heads in two passes of 8
         "mha16": lambda: W.custom(119, Hq=16, Hkv=16, d=128, theta=5e5, span_lens=[[200, 77], [90]],
                                   q_len=[9, 20], ratio=0.3),
+        # NaN / inf in masked slots' K and V and past the sequence's end
+        "masked_garbage": masked_inside_blocks,
     }
 
 
