@@ -190,14 +190,14 @@ __device__ __forceinline__ int task_key0(int wave, int u) {   // first key of (w
     return wave * (64 / GG::PC) + u * (GG::NT / GG::PC);
 }
 
-// Block ids / positions of one tile for this thread's staging tasks, as
-// loaded (at clamped indices); the range check is applied where they are used,
-// one tile later, so that no wait for these loads sits at the tile start.
 // Word 3 of a raw buffer resource on this architecture: 32-bit data format
 // (with a zero format every load would return 0), no swizzle or index stride.
 // A raw load whose byte offset lies past the resource's size returns zeros.
 constexpr int kRsrcWord3 = 0x00020000;
 
+// Block ids / positions of one tile for this thread's staging tasks, as
+// loaded (at clamped indices); the range check is applied where they are used,
+// one tile later, so that no wait for these loads sits at the tile start.
 template <int D, int WAVES>
 struct Meta {
     int32_t kblk[Geo<D, WAVES>::KTASK];   // wave-uniform
@@ -381,13 +381,11 @@ __device__ __forceinline__ int first_bad_key(const FwdParams &p, const int32_t *
 // Rotate and write one tile into an LDS buffer.  With s_bias, also writes
 // each key's score bias (0 if usable, -inf if not); with K rows of unusable
 // keys loaded as zeros their scores are then exactly -inf without a
-// per-score test.  Returns whether every key this thread staged is usable
-// and visible to the workgroup's earliest row.
+// per-score test.
 template <int D, int WAVES, bool ROT>
-__device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uint16_t *Vs, int32_t *s_pi, int tid,
-                                           bool need_v, int min_pos, float *s_bias = nullptr) {
+__device__ __forceinline__ void data_store(Data<D, WAVES> &dt, uint16_t *Ks, uint16_t *Vs, int32_t *s_pi, int tid,
+                                           bool need_v, float *s_bias = nullptr) {
     using GG = Geo<D, WAVES>;
-    bool full = true;
 #pragma unroll
     for (int u = 0; u < GG::KTASK; ++u) {
         const int kk = tid / GG::PC + u * (GG::NT / GG::PC);
@@ -401,7 +399,6 @@ __device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uin
         // masked-path visibility is one compare: unusable keys get INT_MAX
         if (pc == 0) s_pi[kk] = pi >= 0 ? pi : 0x7fffffff;
         if (s_bias && pc == 0) s_bias[kk] = pi >= 0 ? 0.f : -INFINITY;
-        full = full && pi >= 0 && pi <= min_pos;
     }
     if (need_v) {
         int half, dd;
@@ -427,7 +424,6 @@ __device__ __forceinline__ bool data_store(Data<D, WAVES> &dt, uint16_t *Ks, uin
             *reinterpret_cast<u32x4 *>(Vs + voff(d, 2 * b + half)) = v;
         }
     }
-    return full;
 }
 
 // SKIP: skip the tiles whose keys no row of the workgroup sees (launched for
@@ -637,7 +633,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         cs_load<D, WAVES, ROT>(p, dnext, tid);
     }
     if (SKIP ? it0 < ntiles : ntiles > 0) {
-        (void)data_store<D, WAVES, ROT>(dnext, Ks, Vs, s_pi, tid, kV, min_pos, s_bias);
+        data_store<D, WAVES, ROT>(dnext, Ks, Vs, s_pi, tid, kV, s_bias);
         __syncthreads();
     }
     const float sc = p.scale_log2;
@@ -829,9 +825,8 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
             s_red[(cur * WAVES + wave) * kTileN + key] = cs[0];
         }
         if constexpr (MORE)
-            (void)data_store<D, WAVES, ROT>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs + (kV ? (cur ^ 1) * GG::VBUF : 0),
-                                            s_pi + (cur ^ 1) * kTileN, tid, kV, min_pos,
-                                            s_bias + (cur ^ 1) * kTileN);
+            data_store<D, WAVES, ROT>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs + (kV ? (cur ^ 1) * GG::VBUF : 0),
+                                      s_pi + (cur ^ 1) * kTileN, tid, kV, s_bias + (cur ^ 1) * kTileN);
         if constexpr (MODE != kMass) interleave_hint<QG * (D / 16 + 1), 3>();
         __syncthreads();
 
@@ -1083,7 +1078,7 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
     __syncthreads();
     const int first_bad = s_firstbad;
     if (ntiles > 0) {
-        (void)data_store<D, WAVES, ROT>(dnext, Ks, Vs, s_pi, tid, false, min_pos);
+        data_store<D, WAVES, ROT>(dnext, Ks, Vs, s_pi, tid, false);
         __syncthreads();
         data_load<D, WAVES>(p, dnext, m2, g, key_begin + kTileN, key_end, tid, false);
         meta_load<D, WAVES>(m2, bt, pis, key_begin + 2 * kTileN, key_end, tid);
@@ -1160,8 +1155,7 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
             }
         }
         if constexpr (MORE)
-            (void)data_store<D, WAVES, ROT>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs, s_pi + (cur ^ 1) * kTileN, tid, false,
-                                       min_pos);
+            data_store<D, WAVES, ROT>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs, s_pi + (cur ^ 1) * kTileN, tid, false);
         __syncthreads();
         if (tid < kTileN) {
             float tot = 0.f;
