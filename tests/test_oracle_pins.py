@@ -120,10 +120,11 @@ def test_relative_position_form(make):
         assert np.max(np.abs(lse[sl] - l2)) < 1e-10
 
 
-def prerotated_sdpa(w, r):
-    """Rotate keys at pi and queries at t once, with complex multiplication
-    (pair (i, i+d/2) as real and imaginary part), then run textbook attention
-    (torch scaled_dot_product_attention, CPU float64) with a boolean mask."""
+def prerotated(w, r):
+    """Request r rotated once, with complex multiplication (pair (i, i+d/2) as
+    real and imaginary part): queries at t, keys at pi, float64.  Returns
+    Q [Hq, nq, d], K and V [Hq, n, d] (kv heads repeated over their group)
+    and the visibility mask [nq, n]."""
     K, V, pi = gather_dense(w, r)
     d, G = w.head_dim, w.group
     half = d // 2
@@ -143,11 +144,27 @@ def prerotated_sdpa(w, r):
     Kr = Kr.repeat_interleave(G, dim=1)
     Vr = torch.as_tensor(V).repeat_interleave(G, dim=1)
     mask = torch.as_tensor((pi[None, :] >= 0) & (pi[None, :] <= qpos[:, None]))
-    o = torch.nn.functional.scaled_dot_product_attention(
-        Q.transpose(0, 1), Kr.transpose(0, 1), Vr.transpose(0, 1), attn_mask=mask[None])
-    s = (Q.transpose(0, 1) @ Kr.transpose(0, 1).transpose(1, 2)) / math.sqrt(d)
+    return Q.transpose(0, 1), Kr.transpose(0, 1), Vr.transpose(0, 1), mask
+
+
+def prerotated_sdpa(w, r):
+    """Textbook attention (torch scaled_dot_product_attention, CPU float64)
+    with a boolean mask over the once-rotated tensors."""
+    Q, K, V, mask = prerotated(w, r)
+    o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask[None])
+    s = (Q @ K.transpose(1, 2)) / math.sqrt(w.head_dim)
     s = s.masked_fill(~mask[None], -math.inf)
     return o.transpose(0, 1).numpy(), torch.logsumexp(s, -1).transpose(0, 1).numpy()
+
+
+def prerotated_mass(w, r):
+    """Selection mass of request r by another route: torch.softmax over the
+    masked scores of the once-rotated tensors, summed over the request's
+    query tokens and every q head, per slot."""
+    Q, K, _, mask = prerotated(w, r)
+    s = (Q @ K.transpose(1, 2)) / math.sqrt(w.head_dim)
+    p = torch.softmax(s.masked_fill(~mask[None], -math.inf), -1)
+    return torch.nan_to_num(p, nan=0.0).sum((0, 1)).numpy()   # rows that see nothing add nothing
 
 
 @pytest.mark.parametrize("name", ["tiny", "gqa_ragged", "mha"])
@@ -167,6 +184,23 @@ def test_prerotation_equivalence(name):
         sl = slice(w.q_start[r], w.q_start[r + 1])
         assert np.max(np.abs(out[sl] - o2)) < 1e-10
         assert np.max(np.abs(lse[sl] - l2)) < 1e-10
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_mass_equals_summed_softmax_per_slot(seed):
+    """The mass of every slot, not only its total, against the summed
+    probabilities of textbook softmax attention (QCFuse methodology B: the
+    query's attention over the layer's keys scores each token); masked slots
+    hold pi = -1 and get none."""
+    w = W.custom(seed, Hq=6, Hkv=2, d=32, theta=5e5, span_lens=[[40, 17], [30]], gaps=[[0, 500], [3]],
+                 q_len=[5, 3], q_gap=[0, 2])
+    w.kv_pos[0, [3, 20, 41]] = -1
+    mass = oracle.mass(w)
+    for r in range(w.batch):
+        n = int(w.kv_len[r])
+        ref = prerotated_mass(w, r)
+        assert np.max(np.abs(mass[r, :n] - ref)) < 1e-10
+    assert np.all(mass[0, [3, 20, 41]] == 0)
 
 
 def test_identity_positions_is_causal_rope_attention():
