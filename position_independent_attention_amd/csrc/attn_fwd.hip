@@ -8,7 +8,8 @@
 //          selection mass (QCFuse, gist.science 2604.08585, methodology B)
 //
 // Work decomposition
-//   A workgroup (4 x wave64) owns one (request, kv head, key split, row block).
+//   A workgroup (4 or 8 wave64) owns one (request, kv head, key split, row
+//   block).
 //   The G query heads of a kv head are packed with the request's query tokens
 //   into "rows" (row = token * G + head-in-group), so one rotated K tile feeds
 //   G * n_q rows.  Each wave owns 16*QG rows.
@@ -71,6 +72,10 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Finite test on the bit pattern: the kernel sources are built with
+// -fno-honor-nans, under which a float compare may not reject a NaN.
+__device__ __forceinline__ bool finite_bits(float x) { return (__float_as_uint(x) & 0x7fffffffu) < 0x7f800000u; }
 
 #ifndef PIC_SCHED_HINTS
 #define PIC_SCHED_HINTS 0
@@ -562,8 +567,8 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         if constexpr (MODE == kMass) {
             if (qpos[qg] >= 0) {
                 const float ls = p.lse_in[(size_t)qt[qg] * p.hq + qh[qg]];
-                // -inf (nothing visible) or NaN: contribute nothing
-                lse2[qg] = (ls > -INFINITY) ? ls * 1.4426950408889634f : INFINITY;
+                // -inf (nothing visible), +inf or NaN: contribute nothing
+                lse2[qg] = finite_bits(ls) ? ls * 1.4426950408889634f : INFINITY;
             }
         }
     }
@@ -1033,9 +1038,9 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
             const float ls = p.lse_in[(size_t)qt * p.hq + qh];
             if (pos >= p.max_pos) pos = -1;
             rpos[qg][i] = pos;
-            // invalid rows, and rows with nothing visible (-inf) or NaN,
-            // contribute exp2(-inf) = 0
-            lse2[qg][i] = pos >= 0 && ls > -INFINITY ? ls * 1.4426950408889634f : INFINITY;
+            // invalid rows, and rows whose lse is not finite (-inf: nothing
+            // visible; NaN), contribute exp2(-inf) = 0
+            lse2[qg][i] = pos >= 0 && finite_bits(ls) ? ls * 1.4426950408889634f : INFINITY;
         }
     f32x4 s_init[QG];
 #pragma unroll
