@@ -1,9 +1,10 @@
 """HIP path vs the CPU oracle, element by element, through the C ABI.
 
 Bar (tests/util.py): bf16 outputs max abs <= 2e-2 and mean abs <= 2e-3 (plus
-rel-L2 <= 1e-2); LSE abs <= 1e-2; selection mass within 2% + 1e-5; selected
-sets identical outside a 1e-3 band around each span's k-th mass (ties to the
-lower index); fusion bit-exact.  Small shapes compare every output; the full-size shapes compare
+rel-L2 <= 1e-2); the LSE of each row and the selection mass of each slot within
+their own bars from the kernels' bf16 roundings (tests/error_model.py), capped
+at 1e-2 and at 2% + 1e-5; selected sets identical outside a 1e-3 band around
+each span's k-th mass (ties to the lower index); fusion bit-exact.  Small shapes compare every output; the full-size shapes compare
 sampled rows and size-independent properties.
 """
 import dataclasses
@@ -16,7 +17,7 @@ import torch
 import oracle
 from position_independent_attention_amd import pic, workloads as W
 from tests import hip_helpers as H
-from tests.util import (LSE_ABS, check_selection, mass_within, out_within, parity_stats)
+from tests.util import check_lse, check_mass, check_selection, out_within, parity_stats
 
 pytestmark = pytest.mark.gpu
 
@@ -85,7 +86,7 @@ def test_prefill_parity(name):
     out, lse, _ = H.prefill(ctx, w)
     ref_o, ref_l = oracle.attention(w)
     compare_out(H.host_bf16(out), ref_o, "O")
-    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+    check_lse(w, lse.cpu().numpy(), ref_l)
 
 
 def test_prefill_row_without_visible_keys():
@@ -170,7 +171,7 @@ def test_prefill_full_size_sampled(name):
     ref_o, ref_l = oracle.attention(w, (np.array(ts), np.array(hs)))
     o = H.host_bf16(out)[ts, hs]
     compare_out(o, ref_o, "O sampled")
-    assert np.max(np.abs(lse.cpu().numpy()[ts, hs] - ref_l)) <= LSE_ABS
+    check_lse(w, lse.cpu().numpy()[ts, hs], ref_l, rows=(ts, hs))
     assert np.all(np.isfinite(H.host_bf16(out)))
 
 
@@ -212,7 +213,7 @@ def test_decode_parity(name):
     out, lse, _ = H.decode(ctx, w)
     ref_o, ref_l = oracle.attention(w)
     compare_out(H.host_bf16(out), ref_o, "O")
-    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+    check_lse(w, lse.cpu().numpy(), ref_l)
 
 
 def test_decode_full_size_sampled():
@@ -225,7 +226,7 @@ def test_decode_full_size_sampled():
     hs = np.tile(np.arange(w.num_q_heads), len(reqs))
     ref_o, ref_l = oracle.attention(w, (ts, hs))
     compare_out(H.host_bf16(out)[ts, hs], ref_o, "O sampled")
-    assert np.max(np.abs(lse.cpu().numpy()[ts, hs] - ref_l)) <= LSE_ABS
+    check_lse(w, lse.cpu().numpy()[ts, hs], ref_l, rows=(ts, hs))
 
 
 @pytest.mark.parametrize("name", ["one_request_32k", "two_requests_9k"])
@@ -241,7 +242,7 @@ def test_decode_many_splits(name):
     out, lse, _ = H.decode(ctx, w)
     ref_o, ref_l = oracle.attention(w)
     compare_out(H.host_bf16(out), ref_o, "O")
-    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+    check_lse(w, lse.cpu().numpy(), ref_l)
 
 
 def test_decode_matches_prefill_with_one_query():
@@ -291,7 +292,7 @@ def test_decode_irregular_positions(name):
     out, lse, _ = H.decode(ctx, w)
     ref_o, ref_l = oracle.attention(w)
     compare_out(H.host_bf16(out), ref_o, "O")
-    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+    check_lse(w, lse.cpu().numpy(), ref_l)
 
 
 # ------------------------------------------------------------- selection
@@ -316,6 +317,17 @@ def small_select_workloads():
                                   q_len=[9, 20], ratio=0.3),
         # NaN / inf in masked slots' K and V and past the sequence's end
         "masked_garbage": masked_inside_blocks,
+        # the long-context head geometry (32/8, d 128) with more than one
+        # 512-row block of the selection mass pass per kv head, as at the full
+        # shape (1,024 rows): 800 rows (2 blocks) and 1,200 rows (3 blocks, the
+        # last one ragged)
+        "long_context_2rb": lambda: W.long_context(n_spans=3, span_tok=1024, q_len=200),
+        "long_context_3rb": lambda: W.long_context(n_spans=2, span_tok=1024, q_len=300),
+        # d = 64 with 400 and 612 rows per kv head: 2 and 3 of its 256-row blocks
+        "d64_2rb": lambda: W.custom(132, Hq=8, Hkv=2, d=64, theta=1e4, span_lens=[[700, 300]],
+                                    q_len=[100], ratio=0.2),
+        "d64_3rb_batch2": lambda: W.custom(133, Hq=16, Hkv=4, d=64, theta=1e4,
+                                           span_lens=[[500, 333], [900]], q_len=[153, 60], ratio=0.15),
     }
 
 
@@ -326,6 +338,11 @@ def test_select_parity(name, lse_given):
     say(f"select {name} lse_given={lse_given}: spans={len(w.span_req)} ratio={w.ratio}")
     ctx = H.ctx_for(w)
     out, lse, dc = H.prefill(ctx, w)
+    if lse_given and w.total_q * w.num_q_heads >= 4096:
+        # the prefill behind the caller's lse, at the shapes with many row blocks
+        ref_o, ref_l = oracle.attention(w)
+        compare_out(H.host_bf16(out), ref_o, "O")
+        check_lse(w, lse.cpu().numpy(), ref_l)
     sel_off, sel, mass = H.select(ctx, w, dc, lse if lse_given else None)
     ref_m = oracle.mass(w)
     ref_off, ref_idx = oracle.select(w, ref_m)
@@ -336,8 +353,8 @@ def test_select_parity(name, lse_given):
         rel = err / np.maximum(ref_m[r, :n], 1e-12)
         say(f"  mass r{r}: max abs err {err.max():.3e}, max rel err {rel.max():.3e} "
             f"(sum {mass[r, :n].sum():.4f} vs {ref_m[r, :n].sum():.4f})")
-        assert mass_within(mass[r, :n], ref_m[r, :n])
         assert abs(mass[r, :n].astype(np.float64).sum() - ref_m[r, :n].sum()) <= 1e-4 * ref_m[r, :n].sum()
+    check_mass(w, mass, ref_m)
 
 
 def test_select_ties_and_budget_edges():
@@ -437,7 +454,7 @@ def test_fuse_bit_exact_and_second_pass(name):
     out2, lse2, _ = H.prefill(ctx, fused, dc)
     ref2, refl2 = oracle.attention(fused)
     compare_out(H.host_bf16(out2), ref2, "O fused")
-    assert np.max(np.abs(lse2.cpu().numpy() - refl2)) <= LSE_ABS
+    check_lse(fused, lse2.cpu().numpy(), refl2)
 
 
 @pytest.mark.parametrize("d,q_len", [(128, 520), (64, 260)])
@@ -466,7 +483,7 @@ def test_fused_pass_with_many_rows_uses_tile_skipping(d, q_len):
     out, lse, _ = H.prefill(ctx, fused, dc)
     ref_o, ref_l = oracle.attention(fused)
     compare_out(H.host_bf16(out), ref_o, "O fused")
-    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+    check_lse(fused, lse.cpu().numpy(), ref_l)
 
 
 def test_fuse_full_size_with_seeded_selection():
@@ -493,7 +510,7 @@ def test_fuse_full_size_with_seeded_selection():
     hs = np.array([0, 31, 5, 17, 9, 22, 3, 12])
     ref2, refl2 = oracle.attention(fused, (ts, hs))
     compare_out(H.host_bf16(out2)[ts, hs], ref2, "O fused sampled")
-    assert np.max(np.abs(lse2.cpu().numpy()[ts, hs] - refl2)) <= LSE_ABS
+    check_lse(fused, lse2.cpu().numpy()[ts, hs], refl2, rows=(ts, hs))
 
 
 # ------------------------------------------------------- anchor extraction
@@ -586,10 +603,9 @@ def test_prerotated_mode_prefill_and_mass():
     out, lse, dc = H.prefill(ctx, wp)
     ref_o, ref_l = oracle.attention(w)
     compare_out(H.host_bf16(out), ref_o, "O prerotated")
-    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+    check_lse(w, lse.cpu().numpy(), ref_l)
     _, _, mass = H.select(ctx, wp, dc, lse)
-    n = int(w.kv_len[0])
-    assert mass_within(mass[0, :n], oracle.mass(w)[0, :n])
+    check_mass(w, mass, oracle.mass(w))
 
 
 def test_prerotated_mode_decode():
@@ -600,7 +616,7 @@ def test_prerotated_mode_decode():
     out, lse, _ = H.decode(ctx, wp)
     ref_o, ref_l = oracle.attention(w)
     compare_out(H.host_bf16(out), ref_o, "O prerotated decode")
-    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+    check_lse(w, lse.cpu().numpy(), ref_l)
 
 
 # ------------------------------------------------------- sparse recompute
@@ -628,7 +644,7 @@ def test_recompute_parity(name):
     out, lse, _ = H.prefill(ctx, wr)
     ref_o, ref_l = oracle.attention(wr)
     compare_out(H.host_bf16(out), ref_o, "O recompute")
-    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+    check_lse(wr, lse.cpu().numpy(), ref_l)
 
 
 def test_recompute_full_size_sampled():
@@ -645,7 +661,7 @@ def test_recompute_full_size_sampled():
     hs = np.array([0, 31, 5, 17, 9, 22, 3, 12])
     ref_o, ref_l = oracle.attention(wr, (ts, hs))
     compare_out(H.host_bf16(out)[ts, hs], ref_o, "O recompute sampled")
-    assert np.max(np.abs(lse.cpu().numpy()[ts, hs] - ref_l)) <= LSE_ABS
+    check_lse(wr, lse.cpu().numpy()[ts, hs], ref_l, rows=(ts, hs))
 
 
 def test_recompute_skips_tiles_no_row_sees():
@@ -666,7 +682,7 @@ def test_recompute_skips_tiles_no_row_sees():
     out, lse, _ = H.prefill(ctx, wr)
     ref_o, ref_l = oracle.attention(wr)
     compare_out(H.host_bf16(out), ref_o, "O recompute skip")
-    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+    check_lse(wr, lse.cpu().numpy(), ref_l)
 
 
 # ------------------------------------------- span reuse by block hashing
@@ -713,7 +729,7 @@ def test_block_hash_reuse_end_to_end():
     out, lse, _ = H.prefill(ctx, w)
     ref_o, ref_l = oracle.attention(w)
     compare_out(H.host_bf16(out), ref_o, "O block-hash reuse")
-    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= LSE_ABS
+    check_lse(w, lse.cpu().numpy(), ref_l)
     # private copies of request 1's blocks give the same bits
     wp = w.copy()
     n1 = len(maps[1][0])
