@@ -203,6 +203,22 @@ pic_status qc_score_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
                            int32_t max_sel, int32_t *sel_idx, float *mass, void *ws,
                            size_t ws_bytes, void *stream);
 
+/* qc_score_select for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same operation and arguments, with the workspace taken from a scratch
+ * buffer of PIC_NOALLOC_SCRATCH_BYTES that the library holds on each GPU from
+ * the first pic_ctx_create on it until the process ends.  Calls no allocating
+ * routine.  Returns PIC_ERR_WORKSPACE (nothing launched) when the call's
+ * workspace, pic_workspace_bytes(PIC_OP_SELECT), exceeds that size; the
+ * long-context shape (1 request, 33,024 slots, 256 queries, 32/8 heads) needs
+ * under 3 MiB.  All calls on one GPU share the buffer, which keeps the last
+ * call's contents: calls that may overlap on one GPU (other streams, other
+ * host threads) race and must be ordered by the caller. */
+#define PIC_NOALLOC_SCRATCH_BYTES (16u << 20)
+pic_status qc_score_select_noalloc(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_table *req,
+                                   const pic_queries *qs, const float *lse, const pic_spans *spans,
+                                   int32_t max_sel, int32_t *sel_idx, float *mass, void *stream);
+
 /* Anchor extraction ([QCFuse] methodology A, "Extraccion de Anclajes"; phase 1
  * of the German page): the tokens of a context chunk with the highest key
  * norms.  score_r[j] = sum over kv heads g and dims i of k~_j[g][i]^2, the

@@ -8,9 +8,16 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
+
+// Device scratch of qc_score_select_noalloc: one copy per GPU, held until the
+// process ends.  Host code never uses this name as an address (on the host it
+// is only a handle of the symbol); it uses the per-device address that
+// hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[PIC_NOALLOC_SCRATCH_BYTES];
 
 struct pic_ctx {
     int device = 0;
@@ -19,6 +26,7 @@ struct pic_ctx {
     float *sin_d = nullptr;
     double *rev_d = nullptr;      // [d/2] theta^(-2i/d) / (2 pi): revolutions per position
     uint16_t *zero_d = nullptr;   // zero page read in place of unusable keys
+    void *scratch_d = nullptr;    // this device's address of `scratch`
     std::string err;
 };
 
@@ -178,6 +186,26 @@ SelectWs select_ws(const pic_config &c, const FwdPlan &pl, const FwdPlan &plm, i
 
 pic_status check_ctx(const pic_ctx *ctx) { return ctx ? PIC_OK : PIC_ERR_INVALID_ARG; }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (the lookup loads the library's code object there if needed).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(int device, void **out) {
+    *out = nullptr;
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device] = ptr;
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+}
+
 pic_status check_pool_req(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_table *req) {
     if (!pool || !req) return fail(ctx, PIC_ERR_INVALID_ARG, "pool or request table is NULL%s");
     if (!pool->k || !pool->v) return fail(ctx, PIC_ERR_INVALID_ARG, "pool k/v pointer is NULL%s");
@@ -294,6 +322,7 @@ pic_status pic_ctx_create(const pic_config *cfg, pic_ctx **out) {
     const size_t zbytes = (size_t)cfg->head_dim * PIC_BLOCK_SIZE * sizeof(uint16_t);
     if (e == hipSuccess) e = hipMalloc(&ctx->zero_d, zbytes);
     if (e == hipSuccess) e = hipMemset(ctx->zero_d, 0, zbytes);
+    if (e == hipSuccess) e = scratch_address(ctx->device, &ctx->scratch_d);
     if (e != hipSuccess) {
         pic_ctx_destroy(ctx);
         return PIC_ERR_HIP;
@@ -530,6 +559,30 @@ pic_status qc_score_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
         if (e != hipSuccess) return hip_fail(ctx, e, "top-k launch");
     }
     return PIC_OK;
+}
+
+pic_status qc_score_select_noalloc(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_table *req,
+                                   const pic_queries *qs, const float *lse, const pic_spans *spans,
+                                   int32_t max_sel, int32_t *sel_idx, float *mass, void *stream) {
+    if (check_ctx(ctx) != PIC_OK) return PIC_ERR_INVALID_ARG;
+    if (!ctx->scratch_d) return fail(ctx, PIC_ERR_HIP, "no scratch address for this device%s");
+    pic_status st = check_pool_req(ctx, pool, req);
+    if (st != PIC_OK) return st;
+    if ((st = check_queries(ctx, qs, req->batch)) != PIC_OK) return st;
+    const pic_config &c = ctx->cfg;
+    const FwdPlan pl = plan_fwd(c, req->batch, qs->max_q_len, req->max_kv_len);
+    const FwdPlan plm = plan_mass(c, req->batch, qs->max_q_len, req->max_kv_len);
+    const size_t need = select_ws(c, pl, plm, req->batch, req->max_blocks, qs->total_q, req->max_kv_len).total;
+    if (need > (size_t)PIC_NOALLOC_SCRATCH_BYTES) {
+        char buf[160];
+        std::snprintf(buf, sizeof buf, "selection needs %zu bytes of scratch, more than the %zu bytes the "
+                      "no-allocation entry point holds%%s", need, (size_t)PIC_NOALLOC_SCRATCH_BYTES);
+        return fail(ctx, PIC_ERR_WORKSPACE, buf);
+    }
+    // The selection's scratch needs no clearing: every partial the later
+    // kernels read is written first by an earlier kernel of the same call.
+    return qc_score_select(ctx, pool, req, qs, lse, spans, max_sel, sel_idx, mass, ctx->scratch_d,
+                           (size_t)PIC_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 pic_status qc_anchor_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_table *req,

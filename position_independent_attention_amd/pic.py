@@ -91,6 +91,9 @@ def lib() -> C.CDLL:
         h.qc_score_select.argtypes = [_vp, P(PicKvPool), P(PicReqTable), P(PicQueries), _vp, P(PicSpans),
                                       _i32, _vp, _vp, _vp, C.c_size_t, _vp]
         h.qc_score_select.restype = C.c_int
+        h.qc_score_select_noalloc.argtypes = [_vp, P(PicKvPool), P(PicReqTable), P(PicQueries), _vp,
+                                              P(PicSpans), _i32, _vp, _vp, _vp]
+        h.qc_score_select_noalloc.restype = C.c_int
         h.qc_anchor_select.argtypes = [_vp, P(PicKvPool), P(PicReqTable), P(PicSpans), _i32, _vp, _vp, _vp,
                                        C.c_size_t, _vp]
         h.qc_anchor_select.restype = C.c_int
@@ -263,6 +266,16 @@ def qc_score_select(ctx: Context, dc: DeviceCache, lse, max_sel: int, sel_idx, m
     st = lib().qc_score_select(ctx.handle, C.byref(pool), C.byref(req), C.byref(qs), _ptr(lse), C.byref(sp),
                                int(max_sel), _ptr(sel_idx), _ptr(mass), _ptr(ws), ws.numel(), _stream(stream))
     _check(ctx, st, "qc_score_select")
+    return sel_idx, mass
+
+
+def qc_score_select_noalloc(ctx: Context, dc: DeviceCache, lse, max_sel: int, sel_idx, mass=None, stream=None):
+    """qc_score_select with the library's per-GPU scratch as its workspace
+    (no device allocation)."""
+    pool, req, qs, sp = dc.pool(), dc.req(), dc.queries(), dc.spans()
+    st = lib().qc_score_select_noalloc(ctx.handle, C.byref(pool), C.byref(req), C.byref(qs), _ptr(lse),
+                                       C.byref(sp), int(max_sel), _ptr(sel_idx), _ptr(mass), _stream(stream))
+    _check(ctx, st, "qc_score_select_noalloc")
     return sel_idx, mass
 
 
