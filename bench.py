@@ -15,30 +15,49 @@ every step starts from the same cache).
 
 The step is captured once as a HIP graph and replayed once per timed step
 (each replay first checked bit for bit against an eager step); --no-graph
-times it eagerly.  Per-op times come from an eager run with events between
-the calls.
+times it eagerly.  Before any timing the step runs eagerly for
+--clock-warmup-s seconds: the GPU's clock rises over the first tens of
+milliseconds of sustained load, and the W warm-up steps alone may end before
+it settles.  Per-op times come from an eager run with events between the calls.
+The step's working set (~200 MB) stays in the 256 MB Infinity Cache from step
+to step: the headline is a warm figure.
 
 metric: attended KV tokens per second, where each attention-type call over a
 request attends its kv_len minus masked slots (33,024 here) and the step makes
-four such calls.  The roofline object is for the dominant kernel (step 1,
+four such calls.  The roofline object is for the dominant op (step 1,
 MFMA-bound: visible (query, key) pairs x Hq x 4d flops against the bf16 dense
-peak), timed with HIP events on the launch stream.  A decode-heavy line (64
-requests x 16,385 KV slots from 16 shared spans, 64 q / 8 kv heads) reports
-HBM-roofline throughput of pic_attn_decode.  cpu_baseline is the double-
-precision CPU oracle, single-threaded, timed on a sample of step 1's rows and
-scaled by visible (row, key) pairs to the whole step.
+peak), timed with HIP events on the launch stream around the whole
+pic_attn_prefill call (its partials kernel and the split merge).
+
+Other lines (each a single-op timing with HIP events on the launch stream):
+  shared_serving      pic_attn_prefill at 16 requests x 8,320 slots that read one
+                      pool of 64 spans at different offsets (MFMA roofline)
+  selection_64q       qc_score_select with the first 64 query tokens over the
+                      long-context cache (K only: the HBM-leaning selection)
+  decode_heavy        pic_attn_decode, 64 requests x 16,385 slots, 64 q / 8 kv
+                      heads: on 64 private pools of 16 spans (4 GiB, the HBM
+                      roofline) and on 16 shared spans (64 MiB unique, which the
+                      Infinity Cache holds: cache-resident), the latter also
+                      cold (a 1 GiB write evicts the caches before each call)
+  sparse_recompute, anchor_extraction, rotation_ablation, block_hashing
+cpu_baseline: the double-precision CPU oracle on a sample of step 1's rows,
+timed before the GPU is touched, on 1 core and as N processes over
+(kv head, query token) shards, scaled by visible (row, key) pairs to the step.
+measured_peaks: a streaming HBM read, a bf16 MFMA loop and a v_exp_f32 loop on
+the same GPU (libpicpeaks.so); roofline fractions are given against both the
+vendor and the measured peaks.
 
     python bench.py [--steps K] [--warmup W]
 
-HBM traffic of the dominant kernel (roofline.traffic) comes from two
-rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) of this script, each scaled by
-what the same counter reads for a plain device copy of known size
-(--calibrate-copy); --traffic-from turns the four runs into
-profiles/prefill_traffic.json, which records a hash of the kernel sources:
-the field is null once those sources differ from the measured ones.
+HBM traffic (roofline.traffic) comes from two rocprofv3 counter runs
+(FETCH_SIZE, WRITE_SIZE) of this script, each scaled by what the same counter
+reads for a plain device copy of known size (--calibrate-copy);
+--traffic-from turns the four runs into a JSON record under profiles/ holding
+a hash of the kernel sources: the field is null once those sources differ.
 """
 import argparse
 import csv
+import ctypes
 import glob
 import hashlib
 import json
@@ -54,15 +73,19 @@ sys.path.insert(0, ROOT)
 METRIC = "attended KV tokens/s + % of HBM/MFMA roofline (GQA 32q/8kv, d=128)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
 TRAFFIC_KERNEL = "fwd_kernel<128, 2, 8, 0, false, true>"
-# the files whose change invalidates a traffic measurement of that kernel
+# the files whose change invalidates a traffic measurement of a kernel
 TRAFFIC_SOURCES = ["position_independent_attention_amd/csrc/attn_fwd.hip",
+                   "position_independent_attention_amd/csrc/attn_decode.hip",
                    "position_independent_attention_amd/csrc/pic_internal.h",
                    "position_independent_attention_amd/csrc/api.cpp",
                    "position_independent_attention_amd/build.py"]
+PEAKS_LIB = os.path.join(ROOT, "position_independent_attention_amd", "libpicpeaks.so")
 COPY_BYTES = 512 << 20
 ANCHOR_RATIO = 0.05   # anchor fraction per span (the pages say only "a small fraction")
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+MAX_CPU_WORKERS = 16  # the CPU share of one GPU on the GPU hosts
+LINES = ["step", "shared_serving", "selection_64q", "decode", "recompute", "anchor", "ablation", "hashing"]
 
 
 def log(*a):
@@ -80,6 +103,10 @@ def visible_pairs(w):
     return tot
 
 
+def attended_tokens(w):
+    return int(sum(int((w.kv_pos[r, :w.kv_len[r]] >= 0).sum()) for r in range(w.batch)))
+
+
 def sources_hash():
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
@@ -88,11 +115,11 @@ def sources_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """Bytes per launch from profiles/prefill_traffic.json, or None if absent or
-    taken from other kernel sources."""
+def measured_traffic(path=TRAFFIC_FILE):
+    """Bytes per launch from a traffic record, or None if absent or taken from
+    other kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -114,85 +141,223 @@ def calibrate_copy():
     print(json.dumps({"calibration": "device copy", "bytes": COPY_BYTES, "launches": 10}), flush=True)
 
 
-def _pmc(d, counter, name_part, every=1):
+def _pmc(d, counter, name_part, every=1, grid=None):
     """Mean counter value over the dispatches of kernels named like name_part
-    (every: take every n-th of them in dispatch order, from the first).  With
-    every > 1 the dispatches must all have one grid size and come in whole
-    groups of `every`, else the run held other launches of the kernel."""
+    (and with that grid size, if given; every: take every n-th of them in
+    dispatch order, from the first).  With every > 1 the dispatches must all
+    have one grid size and come in whole groups of `every`."""
     rows = []
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
-                rows.append((int(r["Dispatch_Id"]), float(r["Counter_Value"]), r.get("Grid_Size", "")))
+                g = r.get("Grid_Size", "")
+                if grid is None or g == str(grid):
+                    rows.append((int(r["Dispatch_Id"]), float(r["Counter_Value"]), g))
     rows = sorted(rows)
     if every > 1 and (len({g for _, _, g in rows}) > 1 or len(rows) % every):
         raise SystemExit(f"{d}: {len(rows)} dispatches of '{name_part}' with grids {sorted({g for _, _, g in rows})}; "
-                         "profile the step alone (--no-decode --no-recompute --no-anchor --no-ablation --no-hashing)")
+                         "profile one line alone (--only)")
     rows = rows[::every]
     if not rows:
         raise SystemExit(f"no {counter} rows for '{name_part}' under {d}")
     return float(np.mean([v for _, v, _ in rows])), len(rows)
 
 
-def traffic_from(copy_fetch, copy_write, fetch, write):
-    """Scale the kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by the
+def traffic_from(copy_fetch, copy_write, fetch, write, kernel, every, grid, workload, out):
+    """Scale a kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by the
     reading of the same counters for the calibration copy."""
     cf, _ = _pmc(copy_fetch, "FETCH_SIZE", "copyBuffer")
     cw, _ = _pmc(copy_write, "WRITE_SIZE", "copyBuffer")
-    # each step launches the kernel twice (step 1, then the pass over the fused
-    # cache): the step-1 dispatches are every other one from the first
-    kf, nf = _pmc(fetch, "FETCH_SIZE", TRAFFIC_KERNEL, every=2)
-    kw, nw = _pmc(write, "WRITE_SIZE", TRAFFIC_KERNEL, every=2)
+    kf, nf = _pmc(fetch, "FETCH_SIZE", kernel, every=every, grid=grid)
+    kw, nw = _pmc(write, "WRITE_SIZE", kernel, every=every, grid=grid)
     ff, fw = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
-    out = {"kernel": TRAFFIC_KERNEL, "workload": "long_context_qc_fusion step 1 (pic_attn_prefill)",
-           "sources_sha256": sources_hash(),
+    rec = {"kernel": kernel, "grid": grid, "workload": workload, "sources_sha256": sources_hash(),
            "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": COPY_BYTES,
            "fetch_scale": ff, "write_scale": fw,
            "kernel_fetch_kib": kf, "kernel_write_kib": kw, "dispatches": [nf, nw],
            "fetch_bytes_per_launch": kf * 1024.0 * ff, "write_bytes_per_launch": kw * 1024.0 * fw}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as fh:
-        json.dump(out, fh, indent=1)
-    print(json.dumps(out), flush=True)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec), flush=True)
 
 
-def attended_tokens(w):
-    return int(sum(int((w.kv_pos[r, :w.kv_len[r]] >= 0).sum()) for r in range(w.batch)))
+# ------------------------------------------------------------ CPU baseline
+
+_CPU_W = None   # the workload the forked oracle workers read
+
+
+def _oracle_rows(rows):
+    import oracle
+    t, h = rows
+    oracle.attention(_CPU_W, (t, h))
+    return len(t)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baselines(w, one_tokens, all_tokens, step_pairs, step_tokens):
+    """The oracle as it stands, on step 1's first query tokens at the full
+    context: one process on 1 core, then N processes over (kv head, token)
+    shards.  Runs before the GPU is initialised, so the workers are plain
+    forks of a CPU-only process."""
+    import multiprocessing as mp
+    import oracle
+    global _CPU_W
+    _CPU_W = w
+    oracle.lib()
+    G = w.num_q_heads // w.num_kv_heads
+    pi = np.sort(w.kv_pos[0, :w.kv_len[0]][w.kv_pos[0, :w.kv_len[0]] >= 0])
+
+    def pairs_of(nt):
+        return int(np.searchsorted(pi, w.q_pos[:nt], side="right").sum()) * w.num_q_heads
+
+    nt = min(one_tokens, w.total_q)
+    ts = np.repeat(np.arange(nt), w.num_q_heads).astype(np.int32)
+    hs = np.tile(np.arange(w.num_q_heads), nt).astype(np.int32)
+    try:
+        allowed = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {min(allowed)})
+        pinned = True
+    except (AttributeError, OSError):
+        allowed, pinned = None, False
+    c0 = time.perf_counter()
+    oracle.attention(w, (ts, hs))
+    one_s = time.perf_counter() - c0
+    if pinned:
+        os.sched_setaffinity(0, allowed)
+    aff = len(allowed) if allowed else (os.cpu_count() or 1)
+    n = max(1, min(os.cpu_count() or 1, aff, MAX_CPU_WORKERS))
+    na = min(all_tokens, w.total_q)
+    # shards: one kv head's q heads over a contiguous run of tokens
+    shards = []
+    per = max(1, (na * w.num_kv_heads + n - 1) // n)
+    units = [(g, t) for g in range(w.num_kv_heads) for t in range(na)]
+    for s in range(0, len(units), per):
+        chunk = units[s:s + per]
+        t = np.repeat([u[1] for u in chunk], G).astype(np.int32)
+        h = np.concatenate([np.arange(u[0] * G, (u[0] + 1) * G) for u in chunk]).astype(np.int32)
+        shards.append((t, h))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(n) as pool:
+        pool.map(_oracle_rows, [(np.zeros(1, np.int32), np.zeros(1, np.int32))] * n)   # workers up
+        c0 = time.perf_counter()
+        pool.map(_oracle_rows, shards, chunksize=1)
+        all_s = time.perf_counter() - c0
+    one_rate = step_tokens / (one_s * step_pairs / pairs_of(nt))
+    all_rate = step_tokens / (all_s * step_pairs / pairs_of(na))
+    return {
+        "value": round(one_rate, 2), "unit": "attended KV tokens/s", "cores": 1, "kind": "oracle",
+        "sample": f"oracle.attention on {nt} query tokens x {w.num_q_heads} heads of step 1 at the full "
+                  f"33,024-slot context ({one_s:.1f} s, pinned to one core: {pinned}), scaled by visible "
+                  "(row, key) pairs to the whole step",
+        "all_cores": {"value": round(all_rate, 2), "unit": "attended KV tokens/s", "cores": n,
+                      "processes": n, "os_cpu_count": os.cpu_count(), "affinity_cpus": aff,
+                      "cpu_model": cpu_model(),
+                      "sample": f"{na} query tokens x {w.num_q_heads} heads of step 1 in {len(shards)} "
+                                f"(kv head, token) shards over {n} processes ({all_s:.2f} s wall), "
+                                "scaled by visible (row, key) pairs"}}
+
+
+# ------------------------------------------------------------------ peaks
+
+def measure_peaks():
+    if not os.path.exists(PEAKS_LIB):
+        return None
+    h = ctypes.CDLL(PEAKS_LIB)
+    h.pic_peak_hbm_read.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    h.pic_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    h.pic_peak_exp2.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    v = ctypes.c_double(0)
+    out = {}
+    assert h.pic_peak_hbm_read(4 << 30, 5, ctypes.byref(v)) == 0
+    out["hbm_read_gbs"] = round(v.value, 1)
+    best = 0.0
+    for shape, iters in ((16, 20000), (32, 10000)):
+        assert h.pic_peak_mfma_bf16(shape, iters, ctypes.byref(v)) == 0
+        out[f"mfma_bf16_{shape}x{shape}_tflops"] = round(v.value, 1)
+        best = max(best, v.value)
+    out["mfma_bf16_tflops"] = round(best, 1)
+    assert h.pic_peak_exp2(5000, ctypes.byref(v)) == 0
+    out["exp2_gexp_per_s"] = round(v.value, 1)
+    out["what"] = ("streaming read of 4 GiB (16-byte loads), register-resident bf16 MFMA loops at 8 waves per "
+                   "SIMD (best of 16x16x32 and 32x32x16), v_exp_f32 chains; measured on this GPU in this run")
+    return out
+
+
+def roof(bound, achieved, peak, unit, measured_peak=None, **extra):
+    r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4)}
+    if measured_peak:
+        r["measured_peak"] = measured_peak
+        r["frac_of_measured"] = round(achieved / measured_peak, 4)
+    r.update(extra)
+    return r
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    # The GPU's clock rises over the first tens of steps: 3 warm-up steps
-    # time a 20-step loop about 14% slower than the clock settles at.
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--clock-warmup-s", type=float, default=1.0,
+                    help="seconds of eager steps before any timing (the clock settles under load)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16)
+    ap.add_argument("--cpu-all-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-recompute", action="store_true")
-    ap.add_argument("--no-anchor", action="store_true")
-    ap.add_argument("--no-ablation", action="store_true")
-    ap.add_argument("--no-hashing", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--only", default=",".join(LINES),
+                    help="comma-separated lines to run: " + ", ".join(LINES))
     ap.add_argument("--no-graph", action="store_true", help="time the step eagerly, without a HIP graph")
-    ap.add_argument("--decode-private", action="store_true",
-                    help="decode line on the unshared control (4 GiB pool)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the device copy the traffic counters are scaled by")
     ap.add_argument("--traffic-from", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
-                    help="rocprofv3 --pmc output dirs -> profiles/prefill_traffic.json")
+                    help="rocprofv3 --pmc output dirs -> a traffic record (see --traffic-*)")
+    ap.add_argument("--traffic-kernel", default=TRAFFIC_KERNEL)
+    ap.add_argument("--traffic-every", type=int, default=2,
+                    help="take every n-th dispatch of the kernel (the step launches the prefill twice)")
+    ap.add_argument("--traffic-grid", type=int, default=None)
+    ap.add_argument("--traffic-workload", default="long_context_qc_fusion step 1 (pic_attn_prefill)")
+    ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
     args = ap.parse_args()
     if args.traffic_from:
-        traffic_from(*args.traffic_from)
+        traffic_from(*args.traffic_from, args.traffic_kernel, args.traffic_every, args.traffic_grid,
+                     args.traffic_workload, args.traffic_out)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (requests and kv heads "
               "shard without exchange; a split KV range needs one exchange of partial O + LSE); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    only = set(x.strip() for x in args.only.split(",") if x.strip())
+    bad = only - set(LINES)
+    if bad:
+        raise SystemExit(f"unknown --only lines {sorted(bad)}; choose from {LINES}")
+
+    from position_independent_attention_amd import workloads as W
+
+    t0 = time.time()
+    w = W.long_context()
+    log(f"workload built in {time.time() - t0:.1f}s: kv_len {w.max_kv_len}, q {w.total_q}")
+    tokens = attended_tokens(w)
+    step_tokens = 4 * tokens
+    pairs = visible_pairs(w)
+    cpu = None
+    if not args.no_cpu_baseline and not args.calibrate_copy:
+        step_pairs = 3 * pairs * w.num_q_heads + tokens * w.num_q_heads   # 3 prefill-shaped passes + decode
+        cpu = cpu_baselines(w, args.cpu_sample_tokens, args.cpu_all_tokens, step_pairs, step_tokens)
+        log("cpu baseline:", cpu["value"], "1 core;", cpu["all_cores"]["value"], cpu["all_cores"]["cores"], "cores")
 
     import torch
-    from position_independent_attention_amd import pic, workloads as W
+    from position_independent_attention_amd import pic
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibrate_copy:
@@ -200,10 +365,41 @@ def main():
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    peaks = None if args.no_peaks else measure_peaks()
+    if peaks:
+        log("measured peaks:", peaks)
+    mp_tf = peaks["mfma_bf16_tflops"] if peaks else None
+    mp_hbm = peaks["hbm_read_gbs"] if peaks else None
 
-    t0 = time.time()
-    w = W.long_context()
-    log(f"workload built in {time.time() - t0:.1f}s: kv_len {w.max_kv_len}, q {w.total_q}")
+    def settle(fn, seconds):
+        """Run fn back to back for `seconds` (the clock rises under load and
+        drops when the GPU idles, e.g. between timed sections)."""
+        c0, n = time.perf_counter(), 0
+        while time.perf_counter() - c0 < seconds:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            n += 10
+        return n
+
+    def time_calls(fn, reps=10, warm=2, settle_s=0.3):
+        settle(fn, settle_s)
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
     ctx = pic.Context(w.num_q_heads, w.num_kv_heads, w.head_dim, w.rope_theta, w.max_position)
     sel_off = pic.pic_select_offsets(w.span_len, w.ratio)
     nsel = int(sel_off[-1])
@@ -218,10 +414,6 @@ def main():
     dc.kv_pos = state[:npos].view(dc.kv_pos.shape)
     dc.kv_len = state[npos:]
     kv_pos0 = state0[:npos].view(dc.kv_pos.shape)
-
-    def t(a):
-        a = np.ascontiguousarray(a)
-        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
     out1 = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.int16, device=dev)
     lse1 = torch.empty((w.total_q, w.num_q_heads), dtype=torch.float32, device=dev)
@@ -241,7 +433,6 @@ def main():
         pic.pic_workspace_bytes(ctx, pic.PIC_OP_SELECT, dc.req(), dc.total_q, dc.max_q_len),
         pic.pic_workspace_bytes(ctx, pic.PIC_OP_DECODE, req_fused, 0, 0))
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
     names = ["prefill", "select", "fuse", "prefill_fused", "decode"]
 
     def step(evs=None, st=None):
@@ -261,98 +452,100 @@ def main():
         pic.pic_attn_decode(ctx, dcd, q_dec, qpos_dec, out3, None, ws=ws, stream=st)
         if evs: evs[5].record(st)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for k in range(args.steps):
-        step(evs[k])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_eager = start.elapsed_time(stop) / args.steps
-    op_ms = {n: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
-             for i, n in enumerate(names)}
-    log("per-op ms:", {k: round(v, 4) for k, v in op_ms.items()})
+    # clock warm-up: eager steps for a fixed time before anything is timed
+    n_clock = settle(step, args.clock_warmup_s)
+    log(f"clock warm-up: {n_clock} eager steps")
 
-    # The same step captured once as a HIP graph and replayed K times: the step
-    # makes 14 launches, and a replay drops their host-side launch work and most
-    # of the gaps between them.  Every replay is first checked bit for bit
-    # against an eager step (with eager work and synchronisations in between).
-    ms_graph, graph_note = None, "off"
-    if not args.no_graph:
-        outs = (out1, lse1, sel, out2, out3)
-        step()
+    result = {"metric": METRIC, "value": None, "unit": "attended KV tokens/s", "n_gpus": 1,
+              "steps": args.steps, "warmup": args.warmup}
+    if "step" in only:
+        for _ in range(args.warmup):
+            step()
         torch.cuda.synchronize()
-        ref = [o.clone() for o in outs]
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(st=torch.cuda.current_stream())
-        same = True
-        for _ in range(3):
-            for o in outs:
-                o.zero_()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(args.steps):
+            step(evs[k])
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ms_eager = start.elapsed_time(stop) / args.steps
+        op_ms = {n: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+                 for i, n in enumerate(names)}
+        log("per-op ms:", {k: round(v, 4) for k, v in op_ms.items()})
+
+        # The same step captured once as a HIP graph and replayed K times: a
+        # replay drops the launches' host-side work and most of the gaps between
+        # them.  Every replay is first checked bit for bit against an eager step
+        # (with eager work and synchronisations in between).
+        ms_graph, graph_note, n_clock_graph = None, "off", 0
+        if not args.no_graph:
+            outs = (out1, lse1, sel, out2, out3)
+            step()
             torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            same = same and all(torch.equal(o, r) for o, r in zip(outs, ref))
-        if same:
-            for _ in range(args.warmup):
+            ref = [o.clone() for o in outs]
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(st=torch.cuda.current_stream())
+            same = True
+            for _ in range(3):
+                for o in outs:
+                    o.zero_()
+                torch.cuda.synchronize()
                 g.replay()
-            torch.cuda.synchronize()
-            start.record(stream)
-            for _ in range(args.steps):
-                g.replay()
-            stop.record(stream)
-            torch.cuda.synchronize()
-            ms_graph = start.elapsed_time(stop) / args.steps
-            graph_note = "hip graph, one replay per step (replays checked bitwise against an eager step)"
-        else:
-            graph_note = "graph replay differed from the eager step: eager timing reported"
-            log(graph_note)
-        del g
-    ms_per_step = ms_graph if ms_graph is not None else ms_eager
-
-    tokens = attended_tokens(w)
-    step_tokens = 4 * tokens
-    value = step_tokens / (ms_per_step / 1e3)
-    pairs = visible_pairs(w)
-    flops = pairs * w.num_q_heads * 4 * w.head_dim
-    achieved = flops / (op_ms["prefill"] / 1e3) / 1e12
-    roofline = {"kernel": "pic_attn_prefill, step 1: fwd_kernel<128, 2, 8, 0, false, true> (split partials) + merge_kernel; "
-                          "the duration is the whole call's",
-                "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                "algorithmic_flops": flops, "avg_ms": round(op_ms["prefill"], 5)}
-
-    result = {"metric": METRIC, "value": round(value, 1), "unit": "attended KV tokens/s", "n_gpus": 1,
-              "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-              "ms_per_step_eager": round(ms_eager, 5), "launch": graph_note,
-              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-              "data": "synthetic",
-              "config": {"workload": "long_context_qc_fusion", "batch": 1, "kv_slots": int(w.max_kv_len),
-                         "spans": "32 x 1024 reused at shuffled offsets", "query_tokens": int(w.total_q),
-                         "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-                         "rope_theta": w.rope_theta, "select_ratio": w.ratio, "fused_rows": nsel,
-                         "step": "prefill+lse, qc_score_select, kv_fuse_scatter, prefill(fused), decode(1)"},
-              "roofline": roofline, "ops_ms": {k: round(v, 5) for k, v in op_ms.items()}}
-
-    def time_calls(fn, reps=10, warm=2):
-        for _ in range(warm):
-            fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+                torch.cuda.synchronize()
+                same = same and all(torch.equal(o, r) for o, r in zip(outs, ref))
+            if same:
+                # the capture and the checks left the GPU idle: warm up again
+                n_clock_graph = settle(g.replay, args.clock_warmup_s)
+                for _ in range(args.warmup):
+                    g.replay()
+                torch.cuda.synchronize()
+                start.record(stream)
+                for _ in range(args.steps):
+                    g.replay()
+                stop.record(stream)
+                torch.cuda.synchronize()
+                ms_graph = start.elapsed_time(stop) / args.steps
+                graph_note = "hip graph, one replay per step (replays checked bitwise against an eager step)"
+            else:
+                graph_note = "graph replay differed from the eager step: eager timing reported"
+                log(graph_note)
+            del g
+        ms_per_step = ms_graph if ms_graph is not None else ms_eager
+        value = step_tokens / (ms_per_step / 1e3)
+        flops = pairs * w.num_q_heads * 4 * w.head_dim
+        achieved = flops / (op_ms["prefill"] / 1e3) / 1e12
+        result.update({
+            "value": round(value, 1), "ms_per_step": round(ms_per_step, 5),
+            "ms_per_step_eager": round(ms_eager, 5), "launch": graph_note,
+            "clock_warmup": {"seconds": args.clock_warmup_s, "eager_steps": n_clock,
+                             "graph_replays": n_clock_graph if ms_graph is not None else 0,
+                             "what": "untimed steps run back to back for that long before the W warm-up "
+                                     "steps of each timed loop"},
+            "cache_state": "warm: the step's ~200 MB working set stays in the 256 MB Infinity Cache between steps",
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "long_context_qc_fusion", "batch": 1, "kv_slots": int(w.max_kv_len),
+                       "spans": "32 x 1024 reused at shuffled offsets", "query_tokens": int(w.total_q),
+                       "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                       "rope_theta": w.rope_theta, "select_ratio": w.ratio, "fused_rows": nsel,
+                       "step": "prefill+lse, qc_score_select, kv_fuse_scatter, prefill(fused), decode(1)"},
+            "roofline": roof("mfma", achieved, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
+                             traffic=measured_traffic(),
+                             kernel="pic_attn_prefill, step 1: fwd_kernel<128, 2, 8, 0, false, true> (split "
+                                    "partials) + merge_kernel; the duration is the whole call's",
+                             algorithmic_flops=flops, avg_ms=round(op_ms["prefill"], 5)),
+            "ops_ms": {k: round(v, 5) for k, v in op_ms.items()}})
+    else:
+        result.update({"higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                       "data": "synthetic", "config": {"workload": "long_context_qc_fusion"}})
+    if peaks:
+        result["measured_peaks"] = peaks
 
     ablation = None
-    if not args.no_ablation:
+    if "ablation" in only:
         # Rotation-overhead ablation (MiniPIC reports 5.7% end to end): the same
         # prefill call with keys_prerotated = 1, i.e. the keys used as stored.  It
         # runs on the same pool bytes: the kernels' work does not depend on the
@@ -370,7 +563,61 @@ def main():
                                          "overhead": round(t_rot / t_pre - 1.0, 4)}}
         result["rotation_ablation"] = ablation
 
-    if not args.no_recompute:
+    if "selection_64q" in only:
+        # The selection with the first 64 query tokens over the long-context
+        # cache: K only (QCFuse's selection pass reads no V), 256 rows per kv
+        # head, where its work per K byte is near the HBM/MFMA ridge.
+        w64 = W.long_context(q_len=64)
+        s_off = pic.pic_select_offsets(w64.span_len, w64.ratio)
+        n64 = int(s_off[-1])
+        d64 = pic.to_device(w64, dev, sel_off=s_off)
+        o64 = torch.empty((w64.total_q, w64.num_q_heads, w64.head_dim), dtype=torch.int16, device=dev)
+        l64 = torch.empty((w64.total_q, w64.num_q_heads), dtype=torch.float32, device=dev)
+        ws64 = torch.empty(max(pic.pic_workspace_bytes(ctx, pic.PIC_OP_PREFILL, d64.req(), 64, 64),
+                               pic.pic_workspace_bytes(ctx, pic.PIC_OP_SELECT, d64.req(), 64, 64)),
+                           dtype=torch.uint8, device=dev)
+        pic.pic_attn_prefill(ctx, d64, o64, l64, ws=ws64, stream=stream)
+        s64 = torch.empty(n64, dtype=torch.int32, device=dev)
+        sms = time_calls(lambda: pic.qc_score_select(ctx, d64, l64, n64, s64, None, ws=ws64, stream=stream),
+                         reps=20, warm=3)
+        tok64 = attended_tokens(w64)
+        kbytes = tok64 * w64.num_kv_heads * w64.head_dim * 2
+        p64 = visible_pairs(w64)
+        qk_flops = p64 * w64.num_q_heads * 2 * w64.head_dim
+        result["selection_64q"] = {
+            "workload": f"qc_score_select (caller's lse) of 64 query tokens over the {w64.max_kv_len}-slot "
+                        "long-context cache, top 15% per span",
+            "ms_per_call": round(sms, 5), "attended_kv_tokens_per_s": round(tok64 / (sms / 1e3), 1),
+            "roofline": roof("hbm", kbytes / (sms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s", mp_hbm,
+                             algorithmic_bytes=kbytes,
+                             note="K only, read once per call (the mass pass, its column reduction and the "
+                                  "top-k included in the duration)"),
+            "mfma": roof("mfma", qk_flops / (sms / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
+                         algorithmic_flops=qk_flops)}
+        del d64, o64, l64, ws64, s64
+
+    if "shared_serving" in only:
+        # Shared-span serving: 16 requests, each 8 spans of a 64-span pool in its
+        # own order (the same blocks at different offsets), 128 queries each.
+        wss = W.shared_serving()
+        dss = pic.to_device(wss, dev)
+        oss = torch.empty((wss.total_q, wss.num_q_heads, wss.head_dim), dtype=torch.int16, device=dev)
+        lss = torch.empty((wss.total_q, wss.num_q_heads), dtype=torch.float32, device=dev)
+        wsss = torch.empty(max(1, pic.pic_workspace_bytes(ctx, pic.PIC_OP_PREFILL, dss.req(), wss.total_q,
+                                                          wss.max_q_len)), dtype=torch.uint8, device=dev)
+        ms_ss = time_calls(lambda: pic.pic_attn_prefill(ctx, dss, oss, lss, ws=wsss, stream=stream), reps=20)
+        pss = visible_pairs(wss)
+        fl = pss * wss.num_q_heads * 4 * wss.head_dim
+        tss = attended_tokens(wss)
+        result["shared_serving"] = {
+            "workload": "16 requests x 8,320 slots (8 of 64 pooled 1024-token spans each, at their own offsets) "
+                        "+ 128 queries each, 32 q / 8 kv heads, d 128: pic_attn_prefill with lse",
+            "ms_per_call": round(ms_ss, 5), "attended_kv_tokens_per_s": round(tss / (ms_ss / 1e3), 1),
+            "roofline": roof("mfma", fl / (ms_ss / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
+                             algorithmic_flops=fl)}
+        del dss, oss, lss, wsss
+
+    if "recompute" in only:
         # Discrete-token recompute (QCFuse's sparse recompute): the 4,928 selected
         # tokens as queries at their own logical positions over the fused cache.
         step()   # leaves the fused cache and this step's selection in `sel`
@@ -383,17 +630,7 @@ def main():
         outr = torch.empty((nsel, w.num_q_heads, w.head_dim), dtype=torch.int16, device=dev)
         wsr = torch.empty(max(1, pic.pic_workspace_bytes(ctx, pic.PIC_OP_PREFILL, dcr.req(), nsel, nsel)),
                           dtype=torch.uint8, device=dev)
-        for _ in range(2):
-            pic.pic_attn_prefill(ctx, dcr, outr, None, ws=wsr, stream=stream)
-        torch.cuda.synchronize()
-        reps = 10
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            pic.pic_attn_prefill(ctx, dcr, outr, None, ws=wsr, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        rms = e0.elapsed_time(e1) / reps
+        rms = time_calls(lambda: pic.pic_attn_prefill(ctx, dcr, outr, None, ws=wsr, stream=stream))
         fpi = dc.kv_pos.cpu().numpy()[0, :kv_fused]
         fpi = np.sort(fpi[fpi >= 0])
         pairs_r = int(np.searchsorted(fpi, pos_r, side="right").sum())
@@ -402,13 +639,11 @@ def main():
             "workload": f"{nsel} selected tokens as queries at their logical positions over the fused "
                         f"{kv_fused}-slot cache, causal by position",
             "ms_per_call": round(rms, 5), "visible_pairs": pairs_r,
-            "roofline": {"bound": "mfma", "achieved": round(flops_r / (rms / 1e3) / 1e12, 2),
-                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(flops_r / (rms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                         "algorithmic_flops": flops_r}}
+            "roofline": roof("mfma", flops_r / (rms / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
+                             algorithmic_flops=flops_r)}
         del dcr, outr, wsr
 
-    if not args.no_anchor:
+    if "anchor" in only:
         # Anchor extraction: per-span top 5% of slots by stored-key norm over the
         # un-fused long-context cache (reads K once: HBM-bound).
         state.copy_(state0)
@@ -420,67 +655,98 @@ def main():
                               sel_off=t(a_off), n_spans=len(w.span_req))
         asel = torch.empty(max(na, 1), dtype=torch.int32, device=dev)
         anorm = torch.empty(w.kv_pos.shape, dtype=torch.float32, device=dev)
-        for _ in range(3):
-            pic.qc_anchor_select(ctx, dca, na, asel, anorm, stream=stream)
-        torch.cuda.synchronize()
-        reps = 20
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            pic.qc_anchor_select(ctx, dca, na, asel, anorm, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ams = e0.elapsed_time(e1) / reps
+        ams = time_calls(lambda: pic.qc_anchor_select(ctx, dca, na, asel, anorm, stream=stream), reps=20, warm=3)
         kbytes = tokens * w.num_kv_heads * w.head_dim * 2
         result["anchor_extraction"] = {
             "workload": f"{len(w.span_req)} spans x 1024 slots of the long-context cache, top "
                         f"{ANCHOR_RATIO:.0%} per span by key norm ({na} anchors)",
             "ms_per_call": round(ams, 5),
-            "roofline": {"bound": "hbm", "achieved": round(kbytes / (ams / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(kbytes / (ams / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-                         "algorithmic_bytes": kbytes}}
+            "roofline": roof("hbm", kbytes / (ams / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s", mp_hbm,
+                             algorithmic_bytes=kbytes)}
         del dca, asel, anorm
 
-    if not args.no_decode:
-        wd = W.decode_heavy(private_spans=args.decode_private)
-        ctxd = pic.Context(wd.num_q_heads, wd.num_kv_heads, wd.head_dim, wd.rope_theta, wd.max_position)
-        dd = pic.to_device(wd, dev)
-        outd = torch.empty((wd.batch, wd.num_q_heads, wd.head_dim), dtype=torch.int16, device=dev)
-        wsd = torch.empty(max(1, pic.pic_workspace_bytes(ctxd, pic.PIC_OP_DECODE, dd.req(), 0, 0)),
-                          dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            pic.pic_attn_decode(ctxd, dd, dd.q, dd.q_pos, outd, None, ws=wsd, stream=stream)
-        torch.cuda.synchronize()
-        reps = 20
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            pic.pic_attn_decode(ctxd, dd, dd.q, dd.q_pos, outd, None, ws=wsd, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        dms = e0.elapsed_time(e1) / reps
-        if ablation is not None:
-            ctxd_pr = pic.Context(wd.num_q_heads, wd.num_kv_heads, wd.head_dim, wd.rope_theta, wd.max_position,
-                                  keys_prerotated=True)
-            d_pre = time_calls(lambda: pic.pic_attn_decode(ctxd_pr, dd, dd.q, dd.q_pos, outd, None, ws=wsd,
-                                                           stream=stream), reps=20, warm=3)
-            ctxd_pr.close()
-            ablation["decode_heavy_ms"] = {"in_kernel": round(dms, 5), "prerotated": round(d_pre, 5),
-                                           "overhead": round(dms / d_pre - 1.0, 4)}
-        dtok = attended_tokens(wd)
-        kvbytes = dtok * wd.num_kv_heads * wd.head_dim * 2 * 2
-        result["decode_heavy"] = {
-            "workload": "decode_heavy" + ("_private" if args.decode_private else "") +
-                        ": 64 requests x 16,385 KV slots, 64 q / 8 kv heads, d 128",
-            "ms_per_call": round(dms, 5), "attended_kv_tokens_per_s": round(dtok / (dms / 1e3), 1),
-            "roofline": {"bound": "hbm", "achieved": round(kvbytes / (dms / 1e3) / 1e9, 1),
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(kvbytes / (dms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-                         "algorithmic_bytes": kvbytes}}
-        del dd, outd, wsd
-        ctxd.close()
+    if "decode" in only:
+        dlines = {}
+        for private in (True, False):
+            # the private control's 4 GiB pool is drawn on the device (seeded);
+            # its block tables, positions and queries come from the workload
+            wd = W.decode_heavy(private_spans=private, pool_values=not private)
+            ctxd = pic.Context(wd.num_q_heads, wd.num_kv_heads, wd.head_dim, wd.rope_theta, wd.max_position)
+            if private:
+                gen = torch.Generator(device=dev)
+                gen.manual_seed(wd.seed)
+                pk = torch.empty(wd.pool_k.shape, dtype=torch.bfloat16, device=dev)
+                pv = torch.empty(wd.pool_v.shape, dtype=torch.bfloat16, device=dev)
+                for buf in (pk, pv):
+                    flat = buf.view(-1)
+                    for s0 in range(0, flat.numel(), 1 << 28):
+                        n_ = min(1 << 28, flat.numel() - s0)
+                        flat[s0:s0 + n_] = torch.randn(n_, generator=gen, device=dev, dtype=torch.float32)
+                dd = pic.DeviceCache(pk.view(torch.int16), pv.view(torch.int16), t(wd.block_table), t(wd.kv_len),
+                                     t(wd.kv_pos), wd.max_kv_len, q=t(wd.q), q_start=t(wd.q_start),
+                                     q_pos=t(wd.q_pos), total_q=wd.total_q, max_q_len=wd.max_q_len)
+            else:
+                dd = pic.to_device(wd, dev)
+            outd = torch.empty((wd.batch, wd.num_q_heads, wd.head_dim), dtype=torch.int16, device=dev)
+            wsd = torch.empty(max(1, pic.pic_workspace_bytes(ctxd, pic.PIC_OP_DECODE, dd.req(), 0, 0)),
+                              dtype=torch.uint8, device=dev)
+            call = lambda: pic.pic_attn_decode(ctxd, dd, dd.q, dd.q_pos, outd, None, ws=wsd, stream=stream)
+            dms = time_calls(call, reps=20, warm=3)
+            dtok = attended_tokens(wd)
+            kvbytes = dtok * wd.num_kv_heads * wd.head_dim * 2 * 2
+            line = {"ms_per_call": round(dms, 5), "attended_kv_tokens_per_s": round(dtok / (dms / 1e3), 1)}
+            if private:
+                line["workload"] = ("64 requests x 16,385 KV slots, each over 16 spans of its own (a 4 GiB pool, "
+                                    "far above the 256 MB Infinity Cache), 64 q / 8 kv heads, d 128")
+                line["roofline"] = roof("hbm", kvbytes / (dms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s", mp_hbm,
+                                        algorithmic_bytes=kvbytes)
+                dlines["decode_heavy_private"] = line
+            else:
+                line["workload"] = ("64 requests x 16,385 KV slots over the same 16 shared spans at per-request "
+                                    "offsets (64 MiB unique K/V), 64 q / 8 kv heads, d 128")
+                line["roofline"] = roof("cache-resident", kvbytes / (dms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s",
+                                        mp_hbm, algorithmic_bytes=kvbytes,
+                                        note="warm: the 64 MiB of unique K/V stay in the Infinity Cache, so "
+                                             "most algorithmic bytes do not come from HBM; the HBM roofline "
+                                             "is the private-pool line")
+                # cold: a 1 GiB write evicts L2 and the Infinity Cache before each call
+                flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+                cold = []
+                for k in range(12):
+                    flush.fill_(k & 255)
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    call()
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    if k >= 2:
+                        cold.append(a.elapsed_time(b))
+                del flush
+                cms = float(np.median(cold))
+                line["cold"] = {"ms_per_call": round(cms, 5),
+                                "attended_kv_tokens_per_s": round(dtok / (cms / 1e3), 1),
+                                "algorithmic_gbs": round(kvbytes / (cms / 1e3) / 1e9, 1),
+                                "what": "median of 10 calls, each after a 1 GiB device write that evicts the "
+                                        "L2 caches and the Infinity Cache; within a call the 64 requests "
+                                        "re-read the same 64 MiB, so all but the first pass over it come "
+                                        "from the caches again"}
+                if ablation is not None:
+                    ctxd_pr = pic.Context(wd.num_q_heads, wd.num_kv_heads, wd.head_dim, wd.rope_theta,
+                                          wd.max_position, keys_prerotated=True)
+                    d_pre = time_calls(lambda: pic.pic_attn_decode(ctxd_pr, dd, dd.q, dd.q_pos, outd, None,
+                                                                   ws=wsd, stream=stream), reps=20, warm=3)
+                    ctxd_pr.close()
+                    ablation["decode_heavy_ms"] = {"in_kernel": round(dms, 5), "prerotated": round(d_pre, 5),
+                                                   "overhead": round(dms / d_pre - 1.0, 4)}
+                dlines["decode_heavy_shared"] = line
+            del dd, outd, wsd
+            if private:
+                del pk, pv
+            ctxd.close()
+            torch.cuda.empty_cache()
+        result.update(dlines)
 
-    if not args.no_hashing:
+    if "hashing" in only:
         # Span reuse by block hashing (host): 64 requests, each a private prompt
         # and 16 SSEP spans of 1,024 tokens drawn from a pool of 64 spans.
         rng = np.random.default_rng(11)
@@ -492,16 +758,16 @@ def main():
         reqs = []
         for _ in range(64):
             pr = rng.integers(10, 50000, int(rng.integers(16, 200))).tolist()
-            t = pr + [-1] * ((-len(pr)) % bs)
+            tk = pr + [-1] * ((-len(pr)) % bs)
             for k in rng.integers(0, 64, 16):
-                t += pool_sp[int(k)]
-            reqs.append(np.asarray(t, np.int32))
-        ntok = sum(len(t) for t in reqs)
+                tk += pool_sp[int(k)]
+            reqs.append(np.asarray(tk, np.int32))
+        ntok = sum(len(x) for x in reqs)
         cache = pic.BlockCache(200000)
         c0 = time.perf_counter()
         misses = blocks = 0
-        for t in reqs:
-            _, _, m = cache.map_request(t, -1, 1, 2)
+        for x in reqs:
+            _, _, m = cache.map_request(x, -1, 1, 2)
             misses += int(m.sum())
             blocks += len(m)
         hsec = time.perf_counter() - c0
@@ -511,23 +777,8 @@ def main():
                         "pool of 64", "host_ms": round(hsec * 1e3, 3), "tokens_per_s": round(ntok / hsec, 1),
             "blocks": blocks, "reused_blocks": blocks - misses, "where": "host CPU (pic_block_map)"}
 
-    if not args.no_cpu_baseline:
-        import oracle
-        nt = min(args.cpu_sample_tokens, w.total_q)
-        ts = np.repeat(np.arange(nt), w.num_q_heads)
-        hs = np.tile(np.arange(w.num_q_heads), nt)
-        c0 = time.perf_counter()
-        oracle.attention(w, (ts, hs))
-        csec = time.perf_counter() - c0
-        pi = np.sort(w.kv_pos[0, :w.kv_len[0]][w.kv_pos[0, :w.kv_len[0]] >= 0])
-        sample_pairs = int(np.searchsorted(pi, w.q_pos[:nt], side="right").sum()) * w.num_q_heads
-        step_pairs = 3 * pairs * w.num_q_heads + tokens * w.num_q_heads   # 3 prefill-shaped passes + decode
-        cpu_step_s = csec * step_pairs / sample_pairs
-        result["cpu_baseline"] = {
-            "value": round(step_tokens / cpu_step_s, 2), "unit": "attended KV tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"oracle.attention on {nt} query tokens x {w.num_q_heads} heads of step 1 at the full "
-                      f"33,024-slot context ({csec:.1f} s), scaled by visible (row, key) pairs to the whole step"}
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     ctx.close()
     print(json.dumps(result), flush=True)
 

@@ -3,7 +3,8 @@
     python -m position_independent_attention_amd.build
 
 Each translation unit is compiled to an object in _build/ and linked into
-position_independent_attention_amd/libpicattn.so.  Flags: -O3, C++17,
+position_independent_attention_amd/libpicattn.so (the attention library) or
+libpicpeaks.so (machine-peak microbenchmarks for the benchmark).  Flags: -O3, C++17,
 --offload-arch=gfx950, and the packed-fp32 target feature switched off for the
 device code (hipcc's host pass warns that it does not know the feature);
 -fno-honor-nans for the kernel sources; no edge splitting for machine sinking in
@@ -23,6 +24,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpicattn.so")
 SOURCES = ["attn_fwd.hip", "attn_decode.hip", "select_fuse.hip", "api.cpp", "block_hash.cpp"]
+# machine-peak microbenchmarks (the benchmark's measured denominators), a
+# library of their own
+PEAKS_LIB = os.path.join(PKG, "libpicpeaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -60,17 +65,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs: list, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared libraries; returns the path of
+    the attention library."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    with ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PEAKS_SOURCES], PEAKS_LIB)
     return LIB
 
 

@@ -154,11 +154,14 @@ def assemble(name: str, *, seed: int, Hq: int, Hkv: int, d: int, theta: float,
              q_pos0: Sequence[int], n_logical_blocks: int, shared_logical: Sequence[int],
              kv_scale: float = 1.0, ratio: float = 0.25, fuse_cap: Optional[Sequence[int]] = None,
              decode: bool = False, max_position: int = 65536,
-             rng: Optional[np.random.Generator] = None) -> Workload:
+             rng: Optional[np.random.Generator] = None, pool_values: bool = True) -> Workload:
     """Lay pieces out into a paged pool and per-request tables.
 
     Draw order from `rng` (PCG64 seeded with `seed` unless given): block-id
-    permutation, K pool, V pool, q, fresh K, fresh V.  Each request gets
+    permutation, K pool, V pool, q, fresh K, fresh V.  With pool_values=False
+    the K and V pools are not drawn: pool_k / pool_v are read-only zero views
+    of the pool's shape that hold no memory, for callers that fill a pool of
+    that layout themselves (a multi-GiB timing pool drawn on the device).  Each request gets
     `q_len[r]` own query tokens at positions q_pos0[r].., whose (unrotated) K/V
     live in request-private blocks at the end of its sequence, plus
     ceil(fuse_cap[r]/16) more private blocks appended (reserved for fused rows).
@@ -209,10 +212,14 @@ def assemble(name: str, *, seed: int, Hq: int, Hkv: int, d: int, theta: float,
         for i, lb in enumerate(fuse_blocks[r]):
             block_table[r, cur2 // BLOCK + i] = perm[lb]
 
-    pool_k = _normal_bf16(rng, (n_total, Hkv, BLOCK, d), kv_scale)
-    v_tok = _normal_bf16(rng, (n_total, Hkv, BLOCK, d), kv_scale)
-    pool_v = np.ascontiguousarray(v_tok.transpose(0, 1, 3, 2))
-    del v_tok
+    if pool_values:
+        pool_k = _normal_bf16(rng, (n_total, Hkv, BLOCK, d), kv_scale)
+        v_tok = _normal_bf16(rng, (n_total, Hkv, BLOCK, d), kv_scale)
+        pool_v = np.ascontiguousarray(v_tok.transpose(0, 1, 3, 2))
+        del v_tok
+    else:
+        pool_k = np.broadcast_to(np.uint16(0), (n_total, Hkv, BLOCK, d))
+        pool_v = np.broadcast_to(np.uint16(0), (n_total, Hkv, d, BLOCK))
 
     total_q = int(sum(q_len))
     q = _normal_bf16(rng, (total_q, Hq, d))
@@ -317,7 +324,7 @@ def long_context(seed: int = 1004, n_spans: int = 32, span_tok: int = 1024, q_le
 
 
 def decode_heavy(seed: int = 1005, batch: int = 64, n_spans: int = 16, span_tok: int = 1024,
-                 private_spans: bool = False, Hq: int = 64) -> Workload:
+                 private_spans: bool = False, Hq: int = 64, pool_values: bool = True) -> Workload:
     """Batch 64, one query token per request, 16k context built from 16 shared
     1024-token spans in a per-request random order starting at a per-request
     random offset b_r in [0, 1024); 64 q / 8 kv heads, d 128.
@@ -343,7 +350,8 @@ def decode_heavy(seed: int = 1005, batch: int = 64, n_spans: int = 16, span_tok:
     return assemble("decode_heavy_private" if private_spans else "decode_heavy", seed=seed,
                     Hq=Hq, Hkv=8, d=128, theta=5e5, requests=reqs, q_len=[1] * batch,
                     q_pos0=q_pos0, n_logical_blocks=n_log,
-                    shared_logical=range(0 if private_spans else n_log), decode=True, rng=rng)
+                    shared_logical=range(0 if private_spans else n_log), decode=True, rng=rng,
+                    pool_values=pool_values)
 
 
 def custom(seed: int, *, Hq: int, Hkv: int, d: int, theta: float, span_lens: Sequence[Sequence[int]],

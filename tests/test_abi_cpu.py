@@ -76,3 +76,15 @@ def test_entry_points_reject_null_context():
     assert h.qc_anchor_select(None, C.byref(pool), C.byref(req), C.byref(sp), 0, None, None, None, 0, None) == 1
     n = C.c_size_t()
     assert h.pic_workspace_bytes(None, 0, C.byref(req), 0, 0, C.byref(n)) == 1
+
+
+def test_peaks_library_exports_its_header():
+    """libpicpeaks.so (the benchmark's measured peaks) exports every function
+    include/pic_peaks.h declares."""
+    txt = open(os.path.join(ROOT, "include", "pic_peaks.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = sorted(set(re.findall(r"^\s*int\s+(pic_peak_\w+)\s*\(", txt, flags=re.M)))
+    assert names == ["pic_peak_exp2", "pic_peak_hbm_read", "pic_peak_mfma_bf16"], names
+    h = C.CDLL(os.path.join(ROOT, "position_independent_attention_amd", "libpicpeaks.so"))
+    for n in names:
+        assert hasattr(h, n), n
