@@ -93,13 +93,16 @@ FwdPlan plan_fwd(const pic_config &c, int batch, int max_q_len, int max_kv_len) 
 }
 
 // The selection mass pass: at shape >= 1 its workgroups hold twice the rows
-// (4 row tiles per wave: it keeps no O accumulator), and it never skips tiles.
+// (4 row tiles per wave: it keeps no O accumulator), and it never skips
+// tiles.  At d = 128 a request of at most 256 rows per kv head takes 2 row
+// tiles per wave (shape 3): a 512-row workgroup would leave half its waves
+// computing rows that do not exist.
 FwdPlan plan_mass(const pic_config &c, int batch, int max_q_len, int max_kv_len) {
     FwdPlan pl = plan_fwd(c, batch, max_q_len, max_kv_len);
     if (pl.shape == 0) return pl;
     const long long rows = (long long)max_q_len * (c.num_q_heads / c.num_kv_heads);
-    pl.shape = 1;
-    pl.rows_per_block = pic::mass_rows_per_block(c.head_dim);
+    pl.shape = c.head_dim == 128 && rows <= 256 ? 3 : 1;
+    pl.rows_per_block = pic::mass_rows_per_block(c.head_dim, pl.shape);
     pl.row_blocks = (int)((rows + pl.rows_per_block - 1) / pl.rows_per_block);
     set_splits(pl, c, batch, max_kv_len);
     return pl;

@@ -1334,8 +1334,14 @@ template <int D, int MODE>
 hipError_t launch_shape(const FwdParams &p, int shape, hipStream_t s) {
     constexpr bool S = MODE != kMass;
     if (shape == 0) return launch_one<D, 1, 4, MODE, false>(p, s);
-    // the mass pass of larger requests: QG 4 (mass_rows_per_block rows)
-    if constexpr (MODE == kMass) return launch_one<D, 4, D == 128 ? 8 : 4, MODE, false>(p, s);
+    // the mass pass of larger requests: QG 4 (mass_rows_per_block rows), or
+    // QG 2 (shape 3, d = 128: up to 256 rows per kv head)
+    if constexpr (MODE == kMass) {
+        if constexpr (D == 128) {
+            if (shape == 3) return launch_one<D, 2, 8, MODE, false>(p, s);
+        }
+        return launch_one<D, 4, D == 128 ? 8 : 4, MODE, false>(p, s);
+    }
     else if constexpr (D == 128)
         return shape == 2 ? launch_one<D, 2, 8, MODE, S>(p, s) : launch_one<D, 2, 8, MODE, false>(p, s);
     else
@@ -1354,7 +1360,9 @@ hipError_t launch_mode(const FwdParams &p, int mode, int shape, hipStream_t s) {
 }  // namespace
 
 int fwd_rows_per_block(int head_dim, int shape) { return shape == 0 ? 64 : (head_dim == 128 ? 256 : 128); }   // 2 as 1
-int mass_rows_per_block(int head_dim) { return head_dim == 128 ? 512 : 256; }
+int mass_rows_per_block(int head_dim, int shape) {
+    return head_dim == 128 ? (shape == 3 ? 256 : 512) : 256;
+}
 
 hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int shape, hipStream_t s) {
     return head_dim == 64 ? launch_mode<64>(p, mode, shape, s) : launch_mode<128>(p, mode, shape, s);

@@ -136,8 +136,9 @@ struct FuseParams {
 // shape 0: 64 rows per workgroup; shape 1: 256 rows (d = 128) / 128 rows (d = 64);
 // shape 2: shape 1 skipping the tiles that no row of a workgroup sees
 int fwd_rows_per_block(int head_dim, int shape);
-// rows per workgroup of the mass pass at shape >= 1 (4 row tiles per wave)
-int mass_rows_per_block(int head_dim);
+// rows per workgroup of the mass pass at shape >= 1: 4 row tiles per wave, or
+// 2 at shape 3 (d = 128 only)
+int mass_rows_per_block(int head_dim, int shape);
 hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int shape, hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t s);
 hipError_t launch_merge(const MergeParams &p, int head_dim, hipStream_t s);
