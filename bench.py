@@ -72,6 +72,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attended KV tokens/s + % of HBM/MFMA roofline (GQA 32q/8kv, d=128)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+# counter-derived HBM bytes per launch of the other lines' kernels (same format)
+TRAFFIC_RECORDS = {name: os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+                   for name in ("decode_private", "decode_shared", "decode_shared_cold", "mass_long_context",
+                                "mass_selection_64q")}
 TRAFFIC_KERNEL = "fwd_kernel<128, 2, 8, 0, false, true>"
 # the files whose change invalidates a traffic measurement of a kernel
 TRAFFIC_SOURCES = ["position_independent_attention_amd/csrc/attn_fwd.hip",
@@ -141,11 +145,20 @@ def calibrate_copy():
     print(json.dumps({"calibration": "device copy", "bytes": COPY_BYTES, "launches": 10}), flush=True)
 
 
-def _pmc(d, counter, name_part, every=1, grid=None):
+def _parse_slice(text):
+    """'a:b' -> slice(a, b) (either side may be empty or negative)."""
+    if not text:
+        return slice(None)
+    a, _, b = text.partition(":")
+    return slice(int(a) if a else None, int(b) if b else None)
+
+
+def _pmc(d, counter, name_part, every=1, grid=None, part=None):
     """Mean counter value over the dispatches of kernels named like name_part
-    (and with that grid size, if given; every: take every n-th of them in
-    dispatch order, from the first).  With every > 1 the dispatches must all
-    have one grid size and come in whole groups of `every`."""
+    (and with that grid size, if given), in dispatch order: `part` (a slice)
+    of them first, then every n-th from the first.  With every > 1 the
+    dispatches must all have one grid size and come in whole groups of
+    `every`."""
     rows = []
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
@@ -153,7 +166,7 @@ def _pmc(d, counter, name_part, every=1, grid=None):
                 g = r.get("Grid_Size", "")
                 if grid is None or g == str(grid):
                     rows.append((int(r["Dispatch_Id"]), float(r["Counter_Value"]), g))
-    rows = sorted(rows)
+    rows = sorted(rows)[part if part is not None else slice(None)]
     if every > 1 and (len({g for _, _, g in rows}) > 1 or len(rows) % every):
         raise SystemExit(f"{d}: {len(rows)} dispatches of '{name_part}' with grids {sorted({g for _, _, g in rows})}; "
                          "profile one line alone (--only)")
@@ -163,15 +176,17 @@ def _pmc(d, counter, name_part, every=1, grid=None):
     return float(np.mean([v for _, v, _ in rows])), len(rows)
 
 
-def traffic_from(copy_fetch, copy_write, fetch, write, kernel, every, grid, workload, out):
+def traffic_from(copy_fetch, copy_write, fetch, write, kernel, every, grid, workload, out, part_text=""):
     """Scale a kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by the
     reading of the same counters for the calibration copy."""
+    part = _parse_slice(part_text)
     cf, _ = _pmc(copy_fetch, "FETCH_SIZE", "copyBuffer")
     cw, _ = _pmc(copy_write, "WRITE_SIZE", "copyBuffer")
-    kf, nf = _pmc(fetch, "FETCH_SIZE", kernel, every=every, grid=grid)
-    kw, nw = _pmc(write, "WRITE_SIZE", kernel, every=every, grid=grid)
+    kf, nf = _pmc(fetch, "FETCH_SIZE", kernel, every=every, grid=grid, part=part)
+    kw, nw = _pmc(write, "WRITE_SIZE", kernel, every=every, grid=grid, part=part)
     ff, fw = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
     rec = {"kernel": kernel, "grid": grid, "workload": workload, "sources_sha256": sources_hash(),
+           "dispatch_slice": part_text or ":", "every": every,
            "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": COPY_BYTES,
            "fetch_scale": ff, "write_scale": fw,
            "kernel_fetch_kib": kf, "kernel_write_kib": kw, "dispatches": [nf, nw],
@@ -180,6 +195,116 @@ def traffic_from(copy_fetch, copy_write, fetch, write, kernel, every, grid, work
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec), flush=True)
+
+
+# the step's kernels in launch order: (role, name part, launches per step)
+STEP_KERNELS = [("step 1 prefill + step 4 prefill over the fused cache", "fwd_kernel<128, 2, 8, 0, false, true>", 2),
+                ("prefill split merge (steps 1 and 4)", "merge_kernel<128>", 2),
+                ("step 2 mass pass", "mass_kernel<128, 4, 8, true>", 1),
+                ("step 2 column reduction", "mass_reduce_kernel", 1),
+                ("step 2 per-span top-k", "span_topk_kernel", 1),
+                ("step 3 kv_fuse_scatter", "fuse_kernel<128>", 1),
+                ("step 3 kv_len update", "fuse_len_kernel", 1),
+                ("step 5 decode (1 request)", "decode_kernel<128>", 1),
+                ("step 5 decode merge", "merge_many_kernel<128>", 1)]
+
+
+def trace_summary(trace_dir, bench_json):
+    """Per-kernel durations of the long-context step from a rocprofv3 kernel
+    trace of a bench.py run, split by phase with the counts that the run's own
+    JSON line records: the eager timed steps, the timed graph replays and the
+    timed calls of each op's own loop (the loop whose library events give the
+    line's kernels_ms)."""
+    line = None
+    for text in open(bench_json):
+        text = text.strip()
+        if text.startswith("{") and '"metric"' in text:
+            line = json.loads(text)
+    if line is None:
+        raise SystemExit(f"no bench JSON line in {bench_json}")
+    steps, warm = line["steps"], line["warmup"]
+    n_clock = line["clock_warmup"]["eager_steps"]
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    disp = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            disp.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                         int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])))
+    disp.sort()
+
+    def launches(part, grid_of_first=False):
+        ds = [d for d in disp if part in d[1]]
+        if grid_of_first and ds:
+            ds = [d for d in ds if d[3] == ds[0][3]]
+        return np.array([d[2] for d in ds]) / 1e3
+
+    # launches of each of the step's kernels, in order: clock warm-up, warm-up
+    # and timed eager steps, the eager reference of the graph check, 3 checked
+    # replays, clock warm-up replays, warm-up and timed replays; then the
+    # kernel loops (settling, warm-up and timed calls of one op each; the
+    # fused-cache loops come after one more eager step)
+    eager0 = n_clock + warm
+    graph0 = eager0 + steps + 1 + 3 + line["clock_warmup"]["graph_replays"] + warm
+    step_end = graph0 + steps
+    loops = line.get("kernel_loops", {})
+
+    def loop_range(name, before):
+        lp = loops.get(name)
+        if not lp:
+            return None
+        a = before + lp["settle_calls"] + lp["warm"]
+        return a, a + lp["timed"]
+
+    L = {k: (v["settle_calls"] + v["warm"] + v["timed"]) for k, v in loops.items()}
+    # dispatch index ranges of the timed loop calls, per kernel
+    loop_ranges = {
+        "fwd_kernel step 1": loop_range("fwd_kernel step 1", 2 * step_end),
+        "mass_kernel step 2": loop_range("mass_kernel step 2", step_end),
+        "fwd_kernel step 4": loop_range("fwd_kernel step 4", 2 * step_end + L.get("fwd_kernel step 1", 0) + 2)
+        if loops else None,
+        "decode_kernel step 5": loop_range("decode_kernel step 5", step_end + 1),
+    }
+    out = ["| kernel | role | per step | eager timed steps: n / avg us | timed graph replays: n / avg us | "
+           "timed calls of its own loop: n / avg us | library events, same loop: avg us |",
+           "|---|---|---|---|---|---|---|"]
+    kms = line.get("kernels_ms", {})
+
+    def cell(x):
+        return f"{len(x)} / {x.mean():.1f}" if len(x) else "-"
+
+    for role, part, per in STEP_KERNELS:
+        us = launches(part, grid_of_first=part == "decode_kernel<128>")
+        if not len(us):
+            out.append(f"| `{part}` | {role} | {per} | 0 | | | |")
+            continue
+        eg = us[eager0 * per:(eager0 + steps) * per]
+        gr = us[graph0 * per:(graph0 + steps) * per]
+        if per == 2:
+            out.append(f"| `{part}` | {role} | {per} | {cell(eg)} | {cell(gr)} | | |")
+            for k, (name, lname) in enumerate((("first launch of the step", "fwd_kernel step 1"),
+                                               ("second launch of the step", "fwd_kernel step 4"))):
+                rg = loop_ranges.get(lname) if part.startswith("fwd_kernel") else None
+                lp = us[rg[0]:rg[1]] if rg else np.array([])
+                ev = f"{1e3 * kms[lname]:.1f}" if rg and lname in kms else ""
+                out.append(f"| | {name} | 1 | {cell(eg[k::2])} | {cell(gr[k::2])} | {cell(lp) if rg else ''} | "
+                           f"{ev} |")
+        else:
+            lname = {"mass_kernel<128, 4, 8, true>": "mass_kernel step 2",
+                     "decode_kernel<128>": "decode_kernel step 5"}.get(part)
+            rg = loop_ranges.get(lname) if lname else None
+            lp = us[rg[0]:rg[1]] if rg else np.array([])
+            ev = f"{1e3 * kms[lname]:.1f}" if lname in kms else "-"
+            out.append(f"| `{part}` | {role} | {per} | {cell(eg)} | {cell(gr)} | {cell(lp) if rg else ''} | "
+                       f"{ev if rg else ''} |")
+    out.append("")
+    out.append(f"bench line: ms_per_step {line.get('ms_per_step')} (graph), ms_per_step_eager "
+               f"{line.get('ms_per_step_eager')}, ops_ms {json.dumps(line.get('ops_ms'))}; counts: clock warm-up "
+               f"{n_clock} eager steps, {warm} warm-up + {steps} timed eager steps, 1 eager reference + 3 checked "
+               f"replays, {line['clock_warmup']['graph_replays']} clock warm-up replays, {warm} warm-up + {steps} "
+               f"timed replays; kernel loops {json.dumps(loops)}")
+    print("\n".join(out), flush=True)
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -317,6 +442,8 @@ def main():
     ap.add_argument("--only", default=",".join(LINES),
                     help="comma-separated lines to run: " + ", ".join(LINES))
     ap.add_argument("--no-graph", action="store_true", help="time the step eagerly, without a HIP graph")
+    ap.add_argument("--decode-pools", default="private,shared",
+                    help="decode lines to run: private (4 GiB pool), shared (64 MiB pool)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the device copy the traffic counters are scaled by")
     ap.add_argument("--traffic-from", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
@@ -327,10 +454,18 @@ def main():
     ap.add_argument("--traffic-grid", type=int, default=None)
     ap.add_argument("--traffic-workload", default="long_context_qc_fusion step 1 (pic_attn_prefill)")
     ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
+    ap.add_argument("--traffic-slice", default="",
+                    help="python slice 'a:b' of the kernel's dispatches (in order) to average, before --traffic-every")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "BENCH_OUTPUT"),
+                    help="per-phase durations of the step's kernels from a kernel trace of a bench.py run "
+                         "and that run's output")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from, args.traffic_kernel, args.traffic_every, args.traffic_grid,
-                     args.traffic_workload, args.traffic_out)
+                     args.traffic_workload, args.traffic_out, args.traffic_slice)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (requests and kv heads "
@@ -383,18 +518,32 @@ def main():
             n += 10
         return n
 
-    def time_calls(fn, reps=10, warm=2, settle_s=0.3):
-        settle(fn, settle_s)
+    def time_calls(fn, reps=10, warm=2, settle_s=0.3, kctx=None, info=None):
+        """Mean ms per call over `reps` back-to-back calls; with kctx (the
+        calls' context) also the mean ms of the call's main kernel, from the
+        event pair the library has stamped with that kernel's start and end in
+        the same timed loop.  info (a dict)
+        receives the call counts: settling, warm-up, timed."""
+        n_settle = settle(fn, settle_s)
+        if info is not None:
+            info.update(settle_calls=n_settle, warm=warm, timed=reps)
         for _ in range(warm):
             fn()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if kctx is not None:
+            pic.pic_timing_start(kctx, reps)
         a.record(stream)
         for _ in range(reps):
             fn()
         b.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        call_ms = a.elapsed_time(b) / reps
+        if kctx is None:
+            return call_ms
+        kms, _ = pic.pic_timing_stop(kctx, reps)
+        assert len(kms) == reps, (len(kms), reps)
+        return call_ms, float(np.mean(kms))
 
     def t(a):
         a = np.ascontiguousarray(a)
@@ -513,10 +662,32 @@ def main():
                 graph_note = "graph replay differed from the eager step: eager timing reported"
                 log(graph_note)
             del g
+        # The main kernel of each op, timed by the event pair the library has
+        # stamped with its start and end, in back-to-back calls of that op on
+        # the step's own inputs (the
+        # eager step loop above is host-bound on slow hosts: its gaps let the
+        # clock drop).
+        state.copy_(state0)
+        dc.max_kv_len = kv0
+        kern, calls, loops = {}, {}, {}
+        kfns = [("fwd_kernel step 1", lambda: pic.pic_attn_prefill(ctx, dc, out1, lse1, ws=ws, stream=stream)),
+                ("mass_kernel step 2", lambda: pic.qc_score_select(ctx, dc, lse1, nsel, sel, None, ws=ws,
+                                                                   stream=stream)),
+                ("fwd_kernel step 4", lambda: pic.pic_attn_prefill(ctx, dc, out2, None, ws=ws, stream=stream)),
+                ("decode_kernel step 5", lambda: pic.pic_attn_decode(ctx, dcd, q_dec, qpos_dec, out3, None, ws=ws,
+                                                                     stream=stream))]
+        for i, (kname, fn) in enumerate(kfns):
+            if i == 2:
+                step()   # leaves the fused cache
+            loops[kname] = {}
+            calls[kname], kern[kname] = time_calls(fn, reps=args.steps, warm=args.warmup, kctx=ctx,
+                                                   info=loops[kname])
+        log("kernel ms:", {k: round(v, 4) for k, v in kern.items()})
+        kern_ms = kern
         ms_per_step = ms_graph if ms_graph is not None else ms_eager
         value = step_tokens / (ms_per_step / 1e3)
         flops = pairs * w.num_q_heads * 4 * w.head_dim
-        achieved = flops / (op_ms["prefill"] / 1e3) / 1e12
+        achieved = flops / (kern_ms["fwd_kernel step 1"] / 1e3) / 1e12
         result.update({
             "value": round(value, 1), "ms_per_step": round(ms_per_step, 5),
             "ms_per_step_eager": round(ms_eager, 5), "launch": graph_note,
@@ -534,10 +705,20 @@ def main():
                        "step": "prefill+lse, qc_score_select, kv_fuse_scatter, prefill(fused), decode(1)"},
             "roofline": roof("mfma", achieved, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
                              traffic=measured_traffic(),
-                             kernel="pic_attn_prefill, step 1: fwd_kernel<128, 2, 8, 0, false, true> (split "
-                                    "partials) + merge_kernel; the duration is the whole call's",
-                             algorithmic_flops=flops, avg_ms=round(op_ms["prefill"], 5)),
-            "ops_ms": {k: round(v, 5) for k, v in op_ms.items()}})
+                             kernel="fwd_kernel<128, 2, 8, 0, false, true>, step 1 (pic_attn_prefill's split "
+                                    "partials; the merge kernel after it is not included)",
+                             algorithmic_flops=flops, avg_ms=round(kern_ms["fwd_kernel step 1"], 5),
+                             timing=f"HIP events stamped at the kernel's own start and end (the library launches "
+                                    f"it with hipExtLaunchKernelGGL while timing is on), over {args.steps} "
+                                    f"back-to-back step-1 prefill calls",
+                             call=roof("mfma", flops / (calls["fwd_kernel step 1"] / 1e3) / 1e12, PEAK_BF16_TFLOPS,
+                                       "TFLOP/s", mp_tf, avg_ms=round(calls["fwd_kernel step 1"], 5),
+                                       what="the whole pic_attn_prefill call (kernel + split merge), same calls")),
+            "ops_ms": {k: round(v, 5) for k, v in op_ms.items()},
+            "kernels_ms": {k: round(v, 5) for k, v in kern_ms.items()},
+            "kernel_calls_ms": {k: round(v, 5) for k, v in calls.items()},
+            "kernel_loops": loops,
+            "select_mass_kernel_traffic": measured_traffic(TRAFFIC_RECORDS["mass_long_context"])})
     else:
         result.update({"higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                        "data": "synthetic", "config": {"workload": "long_context_qc_fusion"}})
@@ -554,13 +735,17 @@ def main():
         dc.max_kv_len = kv0
         ctx_pr = pic.Context(w.num_q_heads, w.num_kv_heads, w.head_dim, w.rope_theta, w.max_position,
                              keys_prerotated=True)
-        t_rot = time_calls(lambda: pic.pic_attn_prefill(ctx, dc, out1, lse1, ws=ws, stream=stream))
-        t_pre = time_calls(lambda: pic.pic_attn_prefill(ctx_pr, dc, out1, lse1, ws=ws, stream=stream))
+        t_rot, k_rot = time_calls(lambda: pic.pic_attn_prefill(ctx, dc, out1, lse1, ws=ws, stream=stream),
+                                  kctx=ctx)
+        t_pre, k_pre = time_calls(lambda: pic.pic_attn_prefill(ctx_pr, dc, out1, lse1, ws=ws, stream=stream),
+                                  kctx=ctx_pr)
         ctx_pr.close()
         ablation = {"what": "same kernels with keys stored rotated (keys_prerotated = 1) vs rotated in-kernel "
                             "at each key's logical position; timed on the same bytes",
                     "prefill_step1_ms": {"in_kernel": round(t_rot, 5), "prerotated": round(t_pre, 5),
-                                         "overhead": round(t_rot / t_pre - 1.0, 4)}}
+                                         "overhead": round(t_rot / t_pre - 1.0, 4)},
+                    "prefill_step1_kernel_ms": {"in_kernel": round(k_rot, 5), "prerotated": round(k_pre, 5),
+                                                "overhead": round(k_rot / k_pre - 1.0, 4)}}
         result["rotation_ablation"] = ablation
 
     if "selection_64q" in only:
@@ -578,8 +763,8 @@ def main():
                            dtype=torch.uint8, device=dev)
         pic.pic_attn_prefill(ctx, d64, o64, l64, ws=ws64, stream=stream)
         s64 = torch.empty(n64, dtype=torch.int32, device=dev)
-        sms = time_calls(lambda: pic.qc_score_select(ctx, d64, l64, n64, s64, None, ws=ws64, stream=stream),
-                         reps=20, warm=3)
+        sms, skms = time_calls(lambda: pic.qc_score_select(ctx, d64, l64, n64, s64, None, ws=ws64, stream=stream),
+                               reps=20, warm=3, kctx=ctx)
         tok64 = attended_tokens(w64)
         kbytes = tok64 * w64.num_kv_heads * w64.head_dim * 2
         p64 = visible_pairs(w64)
@@ -588,12 +773,16 @@ def main():
             "workload": f"qc_score_select (caller's lse) of 64 query tokens over the {w64.max_kv_len}-slot "
                         "long-context cache, top 15% per span",
             "ms_per_call": round(sms, 5), "attended_kv_tokens_per_s": round(tok64 / (sms / 1e3), 1),
-            "roofline": roof("hbm", kbytes / (sms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s", mp_hbm,
-                             algorithmic_bytes=kbytes,
-                             note="K only, read once per call (the mass pass, its column reduction and the "
-                                  "top-k included in the duration)"),
-            "mfma": roof("mfma", qk_flops / (sms / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
-                         algorithmic_flops=qk_flops)}
+            "roofline": roof("hbm", kbytes / (skms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s", mp_hbm,
+                             algorithmic_bytes=kbytes, avg_ms=round(skms, 5),
+                             traffic=measured_traffic(TRAFFIC_RECORDS["mass_selection_64q"]),
+                             kernel="mass_kernel<128, 2, 8, true> (the mass pass; K only, read once)",
+                             call=roof("hbm", kbytes / (sms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s", mp_hbm,
+                                       avg_ms=round(sms, 5),
+                                       what="the whole qc_score_select call (mass pass, column reduction, "
+                                            "top-k)")),
+            "mfma": roof("mfma", qk_flops / (skms / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
+                         algorithmic_flops=qk_flops, avg_ms=round(skms, 5), kernel="mass_kernel")}
         del d64, o64, l64, ws64, s64
 
     if "shared_serving" in only:
@@ -605,7 +794,8 @@ def main():
         lss = torch.empty((wss.total_q, wss.num_q_heads), dtype=torch.float32, device=dev)
         wsss = torch.empty(max(1, pic.pic_workspace_bytes(ctx, pic.PIC_OP_PREFILL, dss.req(), wss.total_q,
                                                           wss.max_q_len)), dtype=torch.uint8, device=dev)
-        ms_ss = time_calls(lambda: pic.pic_attn_prefill(ctx, dss, oss, lss, ws=wsss, stream=stream), reps=20)
+        ms_ss, k_ss = time_calls(lambda: pic.pic_attn_prefill(ctx, dss, oss, lss, ws=wsss, stream=stream),
+                                 reps=20, kctx=ctx)
         pss = visible_pairs(wss)
         fl = pss * wss.num_q_heads * 4 * wss.head_dim
         tss = attended_tokens(wss)
@@ -613,8 +803,10 @@ def main():
             "workload": "16 requests x 8,320 slots (8 of 64 pooled 1024-token spans each, at their own offsets) "
                         "+ 128 queries each, 32 q / 8 kv heads, d 128: pic_attn_prefill with lse",
             "ms_per_call": round(ms_ss, 5), "attended_kv_tokens_per_s": round(tss / (ms_ss / 1e3), 1),
-            "roofline": roof("mfma", fl / (ms_ss / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
-                             algorithmic_flops=fl)}
+            "roofline": roof("mfma", fl / (k_ss / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
+                             algorithmic_flops=fl, avg_ms=round(k_ss, 5), kernel="the prefill kernel",
+                             call=roof("mfma", fl / (ms_ss / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
+                                       avg_ms=round(ms_ss, 5), what="the whole pic_attn_prefill call"))}
         del dss, oss, lss, wsss
 
     if "recompute" in only:
@@ -630,7 +822,8 @@ def main():
         outr = torch.empty((nsel, w.num_q_heads, w.head_dim), dtype=torch.int16, device=dev)
         wsr = torch.empty(max(1, pic.pic_workspace_bytes(ctx, pic.PIC_OP_PREFILL, dcr.req(), nsel, nsel)),
                           dtype=torch.uint8, device=dev)
-        rms = time_calls(lambda: pic.pic_attn_prefill(ctx, dcr, outr, None, ws=wsr, stream=stream))
+        rms, krms = time_calls(lambda: pic.pic_attn_prefill(ctx, dcr, outr, None, ws=wsr, stream=stream),
+                               kctx=ctx)
         fpi = dc.kv_pos.cpu().numpy()[0, :kv_fused]
         fpi = np.sort(fpi[fpi >= 0])
         pairs_r = int(np.searchsorted(fpi, pos_r, side="right").sum())
@@ -639,8 +832,11 @@ def main():
             "workload": f"{nsel} selected tokens as queries at their logical positions over the fused "
                         f"{kv_fused}-slot cache, causal by position",
             "ms_per_call": round(rms, 5), "visible_pairs": pairs_r,
-            "roofline": roof("mfma", flops_r / (rms / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
-                             algorithmic_flops=flops_r)}
+            "roofline": roof("mfma", flops_r / (krms / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
+                             algorithmic_flops=flops_r, avg_ms=round(krms, 5),
+                             kernel="fwd_kernel<128, 2, 8, 0, true, true> (tile skipping)",
+                             call=roof("mfma", flops_r / (rms / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
+                                       avg_ms=round(rms, 5), what="the whole pic_attn_prefill call"))}
         del dcr, outr, wsr
 
     if "anchor" in only:
@@ -667,7 +863,8 @@ def main():
 
     if "decode" in only:
         dlines = {}
-        for private in (True, False):
+        pools = [x.strip() for x in args.decode_pools.split(",") if x.strip()]
+        for private in [x == "private" for x in pools]:
             # the private control's 4 GiB pool is drawn on the device (seeded);
             # its block tables, positions and queries come from the workload
             wd = W.decode_heavy(private_spans=private, pool_values=not private)
@@ -691,24 +888,36 @@ def main():
             wsd = torch.empty(max(1, pic.pic_workspace_bytes(ctxd, pic.PIC_OP_DECODE, dd.req(), 0, 0)),
                               dtype=torch.uint8, device=dev)
             call = lambda: pic.pic_attn_decode(ctxd, dd, dd.q, dd.q_pos, outd, None, ws=wsd, stream=stream)
-            dms = time_calls(call, reps=20, warm=3)
+            dms, kdms = time_calls(call, reps=20, warm=3, kctx=ctxd)
             dtok = attended_tokens(wd)
             kvbytes = dtok * wd.num_kv_heads * wd.head_dim * 2 * 2
-            line = {"ms_per_call": round(dms, 5), "attended_kv_tokens_per_s": round(dtok / (dms / 1e3), 1)}
+            line = {"ms_per_call": round(dms, 5), "attended_kv_tokens_per_s": round(dtok / (dms / 1e3), 1),
+                    "kernel_ms": round(kdms, 5)}
+            dcall = dict(avg_ms=round(dms, 5), what="the whole pic_attn_decode call (kernel + split merge)")
             if private:
                 line["workload"] = ("64 requests x 16,385 KV slots, each over 16 spans of its own (a 4 GiB pool, "
                                     "far above the 256 MB Infinity Cache), 64 q / 8 kv heads, d 128")
-                line["roofline"] = roof("hbm", kvbytes / (dms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s", mp_hbm,
-                                        algorithmic_bytes=kvbytes)
+                line["roofline"] = roof("hbm", kvbytes / (kdms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s", mp_hbm,
+                                        algorithmic_bytes=kvbytes, avg_ms=round(kdms, 5),
+                                        kernel="decode_kernel<128>",
+                                        traffic=measured_traffic(TRAFFIC_RECORDS["decode_private"]),
+                                        call=roof("hbm", kvbytes / (dms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s",
+                                                  mp_hbm, **dcall))
                 dlines["decode_heavy_private"] = line
             else:
                 line["workload"] = ("64 requests x 16,385 KV slots over the same 16 shared spans at per-request "
                                     "offsets (64 MiB unique K/V), 64 q / 8 kv heads, d 128")
-                line["roofline"] = roof("cache-resident", kvbytes / (dms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s",
-                                        mp_hbm, algorithmic_bytes=kvbytes,
+                line["roofline"] = roof("cache-resident", kvbytes / (kdms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s",
+                                        mp_hbm, algorithmic_bytes=kvbytes, avg_ms=round(kdms, 5),
+                                        kernel="decode_kernel<128>",
+                                        traffic=measured_traffic(TRAFFIC_RECORDS["decode_shared"]),
+                                        call=roof("cache-resident", kvbytes / (dms / 1e3) / 1e9, PEAK_HBM_GBS,
+                                                  "GB/s", mp_hbm, **dcall),
                                         note="warm: the 64 MiB of unique K/V stay in the Infinity Cache, so "
                                              "most algorithmic bytes do not come from HBM; the HBM roofline "
-                                             "is the private-pool line")
+                                             "is the private-pool line.  traffic (FETCH_SIZE + WRITE_SIZE) "
+                                             "counts what the L2 fetches from beyond it: the Infinity Cache "
+                                             "or HBM")
                 # cold: a 1 GiB write evicts L2 and the Infinity Cache before each call
                 flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
                 cold = []
@@ -726,6 +935,7 @@ def main():
                 line["cold"] = {"ms_per_call": round(cms, 5),
                                 "attended_kv_tokens_per_s": round(dtok / (cms / 1e3), 1),
                                 "algorithmic_gbs": round(kvbytes / (cms / 1e3) / 1e9, 1),
+                                "traffic": measured_traffic(TRAFFIC_RECORDS["decode_shared_cold"]),
                                 "what": "median of 10 calls, each after a 1 GiB device write that evicts the "
                                         "L2 caches and the Infinity Cache; within a call the 64 requests "
                                         "re-read the same 64 MiB, so all but the first pass over it come "

@@ -144,15 +144,38 @@ typedef struct {
 } pic_spans;
 
 /* Create a context on the current HIP device: validates the config and builds
- * the RoPE cos/sin table (computed in double on the host, stored as fp32 on
- * the device: 2 * max_position * d/2 * 4 bytes).  *out is NULL on failure. */
+ * the RoPE cos/sin table that the kernels read at each key's logical position
+ * ([MiniPIC] section 2.1, implementation notes: the rotation is applied inside
+ * the attention kernel from a cos/sin table).  The table is computed in
+ * double on the host and stored as fp32 on the device
+ * (2 * max_position * d/2 * 4 bytes).  *out is NULL on failure. */
 pic_status pic_ctx_create(const pic_config *cfg, pic_ctx **out);
 void pic_ctx_destroy(pic_ctx *ctx);
 const char *pic_status_str(pic_status s);
 /* Text of the last error recorded on ctx ("" if none). */
 const char *pic_ctx_last_error(const pic_ctx *ctx);
 
+/* Kernel timing, for benchmarks.  pic_timing_start creates 2 * capacity HIP
+ * events (1 <= capacity <= 65536) on the context's device and switches
+ * timing on.  While it is on, each pic_attn_prefill, pic_attn_decode and
+ * qc_score_select call launches its main kernel (the prefill kernel without
+ * the split merge, the decode kernel without its merge, the selection's mass
+ * pass without the column reduction and the top-k) with an event pair that
+ * HIP stamps at that kernel's own start and end (hipExtLaunchKernelGGL),
+ * until capacity intervals are held; later calls run untimed.  pic_timing_stop waits for the last recorded event,
+ * writes the first min(cap, count) intervals in call order (ms: elapsed
+ * milliseconds; ops: the pic_op of the call, either array may be NULL),
+ * sets *count to the number of intervals recorded, destroys the events and
+ * switches timing off.  Do not capture a stream into a graph, nor call from
+ * several threads, while timing is on.  Errors: PIC_ERR_INVALID_ARG if
+ * timing is already on (start) or off (stop), PIC_ERR_HIP if an event
+ * cannot be created or read. */
+pic_status pic_timing_start(pic_ctx *ctx, int32_t capacity);
+pic_status pic_timing_stop(pic_ctx *ctx, float *ms, int32_t *ops, int32_t cap, int32_t *count);
+
 /* Bytes of device workspace that `op` needs for these sizes (0 is possible).
+ * The pages specify no workspace: this is the library's own scratch for the
+ * split-KV partials, the selection's mass partials and the like.
  * For PIC_OP_DECODE total_q and max_q_len are ignored (one query per request).
  * For PIC_OP_SELECT the figure covers the case lse == NULL and mass == NULL.
  * For PIC_OP_ANCHOR total_q and max_q_len are ignored; the figure covers
@@ -251,7 +274,8 @@ pic_status qc_anchor_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req
  * Precondition: block_table[r][base/16 ..] already names request-private
  * blocks with room for the rows; a block id outside [0, num_blocks) is
  * skipped.  n_sel = sel_req_off[batch] (host value).  max_rows_per_req is a
- * host bound of sel_req_off[r+1] - sel_req_off[r]. */
+ * host bound of sel_req_off[r+1] - sel_req_off[r].  Returns
+ * PIC_ERR_UNSUPPORTED for batch > 65535. */
 pic_status kv_fuse_scatter(pic_ctx *ctx, pic_kv_pool *pool, pic_req_table *req,
                            const int32_t *sel_idx, const int32_t *sel_req_off,
                            const uint16_t *k_new, const uint16_t *v_new, int32_t n_sel,

@@ -1,7 +1,8 @@
 // Host side of the C ABI declared in include/pic_attn.h: context and RoPE
 // table, argument validation, launch planning, workspace carving and the
-// launches of the gfx950 kernels.  No entry point allocates except
-// pic_ctx_create; no entry point synchronises the stream.
+// launches of the gfx950 kernels.  No entry point allocates device memory
+// except pic_ctx_create (pic_timing_start creates HIP events); no entry
+// point synchronises the stream except pic_timing_stop.
 #include "pic_attn.h"
 #include "pic_internal.h"
 
@@ -28,6 +29,10 @@ struct pic_ctx {
     uint16_t *zero_d = nullptr;   // zero page read in place of unusable keys
     void *scratch_d = nullptr;    // this device's address of `scratch`
     std::string err;
+    // kernel timing (pic_timing_start / pic_timing_stop): event pairs in call order
+    bool timing = false;
+    std::vector<hipEvent_t> tev;  // 2 * capacity
+    std::vector<int32_t> top;     // op of each recorded interval
 };
 
 namespace {
@@ -189,6 +194,23 @@ SelectWs select_ws(const pic_config &c, const FwdPlan &pl, const FwdPlan &plm, i
 
 pic_status check_ctx(const pic_ctx *ctx) { return ctx ? PIC_OK : PIC_ERR_INVALID_ARG; }
 
+// Kernel timing: the next free event pair (if timing is on and the capacity
+// holds another interval), stamped by the launch with the main kernel's own
+// start and end; the interval counts once the launch has succeeded.
+struct TimedSpan {
+    pic_ctx *ctx;
+    pic_op op;
+    pic::KernelEvents ev;
+    TimedSpan(pic_ctx *c, pic_op o) : ctx(c), op(o) {
+        if (!ctx->timing || ctx->top.size() * 2 >= ctx->tev.size()) return;
+        ev.start = ctx->tev[2 * ctx->top.size()];
+        ev.stop = ctx->tev[2 * ctx->top.size() + 1];
+    }
+    void commit() {
+        if (ev.start) ctx->top.push_back((int32_t)op);
+    }
+};
+
 // Device address of `scratch` on the current device, looked up once per
 // device (the lookup loads the library's code object there if needed).
 constexpr int kMaxDevices = 64;
@@ -336,11 +358,55 @@ pic_status pic_ctx_create(const pic_config *cfg, pic_ctx **out) {
 
 void pic_ctx_destroy(pic_ctx *ctx) {
     if (!ctx) return;
+    for (hipEvent_t ev : ctx->tev) (void)hipEventDestroy(ev);
     if (ctx->cos_d) (void)hipFree(ctx->cos_d);
     if (ctx->sin_d) (void)hipFree(ctx->sin_d);
     if (ctx->rev_d) (void)hipFree(ctx->rev_d);
     if (ctx->zero_d) (void)hipFree(ctx->zero_d);
     delete ctx;
+}
+
+pic_status pic_timing_start(pic_ctx *ctx, int32_t capacity) {
+    if (check_ctx(ctx) != PIC_OK) return PIC_ERR_INVALID_ARG;
+    if (ctx->timing) return fail(ctx, PIC_ERR_INVALID_ARG, "timing is already on%s");
+    if (capacity < 1 || capacity > 65536) return fail(ctx, PIC_ERR_INVALID_ARG, "timing capacity out of range%s");
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != ctx->device) e = hipSetDevice(ctx->device);
+    ctx->tev.assign(2 * (size_t)capacity, nullptr);
+    for (size_t i = 0; e == hipSuccess && i < ctx->tev.size(); ++i) e = hipEventCreate(&ctx->tev[i]);
+    if (cur != ctx->device) (void)hipSetDevice(cur);
+    if (e != hipSuccess) {
+        for (hipEvent_t ev : ctx->tev)
+            if (ev) (void)hipEventDestroy(ev);
+        ctx->tev.clear();
+        return hip_fail(ctx, e, "timing events");
+    }
+    ctx->top.clear();
+    ctx->top.reserve(capacity);
+    ctx->timing = true;
+    return PIC_OK;
+}
+
+pic_status pic_timing_stop(pic_ctx *ctx, float *ms, int32_t *ops, int32_t cap, int32_t *count) {
+    if (check_ctx(ctx) != PIC_OK) return PIC_ERR_INVALID_ARG;
+    if (!ctx->timing) return fail(ctx, PIC_ERR_INVALID_ARG, "timing is off%s");
+    if (cap < 0 || !count) return fail(ctx, PIC_ERR_INVALID_ARG, "cap / count invalid%s");
+    const int32_t n = (int32_t)ctx->top.size();
+    hipError_t e = n > 0 ? hipEventSynchronize(ctx->tev[2 * (size_t)n - 1]) : hipSuccess;
+    for (int32_t i = 0; e == hipSuccess && i < n && i < cap; ++i) {
+        float t = 0.f;
+        e = hipEventElapsedTime(&t, ctx->tev[2 * (size_t)i], ctx->tev[2 * (size_t)i + 1]);
+        if (ms) ms[i] = t;
+        if (ops) ops[i] = ctx->top[i];
+    }
+    for (hipEvent_t ev : ctx->tev) (void)hipEventDestroy(ev);
+    ctx->tev.clear();
+    ctx->top.clear();
+    ctx->timing = false;
+    *count = n;
+    if (e != hipSuccess) return hip_fail(ctx, e, "timing read");
+    return PIC_OK;
 }
 
 // Anchor extraction: the per-slot score when the caller passes no buffer.
@@ -415,8 +481,10 @@ pic_status pic_attn_prefill(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req
         p.part_o = (float *)((char *)ws + w.part_o);
         p.part_ml = (float *)((char *)ws + w.part_ml);
     }
-    hipError_t e = pic::launch_fwd(p, c.head_dim, pic::kAttn, pl.shape, s);
+    TimedSpan ts(ctx, PIC_OP_PREFILL);
+    hipError_t e = pic::launch_fwd(p, c.head_dim, pic::kAttn, pl.shape, s, ts.ev);
     if (e != hipSuccess) return hip_fail(ctx, e, "prefill launch");
+    ts.commit();
     if (pl.num_splits > 1) {
         pic::MergeParams m{p.part_o, p.part_ml, pl.num_splits, qs->total_q * c.num_q_heads, out, lse};
         e = pic::launch_merge(m, c.head_dim, s);
@@ -473,8 +541,10 @@ pic_status pic_attn_decode(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
         p.part_o = (float *)((char *)ws + w.part_o);
         p.part_ml = (float *)((char *)ws + w.part_ml);
     }
-    hipError_t e = pic::launch_decode(p, c.head_dim, s);
+    TimedSpan ts(ctx, PIC_OP_DECODE);
+    hipError_t e = pic::launch_decode(p, c.head_dim, s, ts.ev);
     if (e != hipSuccess) return hip_fail(ctx, e, "decode launch");
+    ts.commit();
     if (splits > 1) {
         pic::MergeParams m{p.part_o, p.part_ml, splits, req->batch * c.num_q_heads, out, lse};
         e = pic::launch_merge(m, c.head_dim, s);
@@ -552,8 +622,10 @@ pic_status qc_score_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
         pm.split_len = plm.split_len;
         pm.num_splits = plm.num_splits;
         pm.row_blocks = plm.row_blocks;
-        e = pic::launch_fwd(pm, c.head_dim, pic::kMass, plm.shape, s);
+        TimedSpan ts(ctx, PIC_OP_SELECT);
+        e = pic::launch_fwd(pm, c.head_dim, pic::kMass, plm.shape, s, ts.ev);
         if (e != hipSuccess) return hip_fail(ctx, e, "selection mass launch");
+        ts.commit();
     }
     e = pic::launch_mass_reduce(sp, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "mass reduce launch");
@@ -649,6 +721,7 @@ pic_status kv_fuse_scatter(pic_ctx *ctx, pic_kv_pool *pool, pic_req_table *req, 
     if (n_sel < 0 || max_rows_per_req < 0 || max_rows_per_req > n_sel)
         return fail(ctx, PIC_ERR_INVALID_ARG, "n_sel / max_rows_per_req invalid%s");
     if (req->batch > 0 && !sel_req_off) return fail(ctx, PIC_ERR_INVALID_ARG, "sel_req_off is NULL%s");
+    if (req->batch > 65535) return fail(ctx, PIC_ERR_UNSUPPORTED, "kv_fuse_scatter supports up to 65535 requests%s");
     if (n_sel > 0 && (!sel_idx || !k_new || !v_new))
         return fail(ctx, PIC_ERR_INVALID_ARG, "sel_idx / k_new / v_new is NULL%s");
     if (req->batch == 0) return PIC_OK;

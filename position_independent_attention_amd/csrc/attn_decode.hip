@@ -393,13 +393,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t s) {
+hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t s, KernelEvents ev) {
     const int nwg = p.hkv * p.num_splits * p.batch;
     if (nwg <= 0) return hipSuccess;
-    if (head_dim == 64)
-        hipLaunchKernelGGL(decode_kernel<64>, dim3(nwg), dim3(kThreads), 0, s, p);
+    auto k = head_dim == 64 ? decode_kernel<64> : decode_kernel<128>;
+    if (ev.start)
+        hipExtLaunchKernelGGL(k, dim3(nwg), dim3(kThreads), 0, s, ev.start, ev.stop, 0, p);
     else
-        hipLaunchKernelGGL(decode_kernel<128>, dim3(nwg), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(k, dim3(nwg), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -1312,17 +1312,19 @@ __global__ __launch_bounds__(256) void merge_many_kernel(MergeParams p) {
 // no table row is read.  A compile-time choice, so that no branch splits the
 // MFMA / VALU regions of the tile loop.
 template <int D, int QG, int WAVES, int MODE, bool SKIP>
-hipError_t launch_one(const FwdParams &p, hipStream_t s) {
+hipError_t launch_one(const FwdParams &p, hipStream_t s, const KernelEvents &ev) {
     const int nwg = p.row_blocks * p.hkv * p.num_splits * p.batch;
     if (nwg <= 0) return hipSuccess;
     const dim3 grid(nwg), block(64 * WAVES);
-    if constexpr (MODE == kMass && QG % 2 == 0) {
-        if (p.rotate_k) hipLaunchKernelGGL((mass_kernel<D, QG, WAVES, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((mass_kernel<D, QG, WAVES, false>), grid, block, 0, s, p);
-    } else {
-        if (p.rotate_k) hipLaunchKernelGGL((fwd_kernel<D, QG, WAVES, MODE, SKIP, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((fwd_kernel<D, QG, WAVES, MODE, SKIP, false>), grid, block, 0, s, p);
-    }
+    void (*k)(FwdParams);
+    if constexpr (MODE == kMass && QG % 2 == 0)
+        k = p.rotate_k ? mass_kernel<D, QG, WAVES, true> : mass_kernel<D, QG, WAVES, false>;
+    else
+        k = p.rotate_k ? fwd_kernel<D, QG, WAVES, MODE, SKIP, true> : fwd_kernel<D, QG, WAVES, MODE, SKIP, false>;
+    if (ev.start)
+        hipExtLaunchKernelGGL(k, grid, block, 0, s, ev.start, ev.stop, 0, p);
+    else
+        hipLaunchKernelGGL(k, grid, block, 0, s, p);
     return hipGetLastError();
 }
 
@@ -1331,29 +1333,29 @@ hipError_t launch_one(const FwdParams &p, hipStream_t s) {
 // shape 2 = shape 1 that skips tiles no row of the workgroup sees (not in
 // mass mode).
 template <int D, int MODE>
-hipError_t launch_shape(const FwdParams &p, int shape, hipStream_t s) {
+hipError_t launch_shape(const FwdParams &p, int shape, hipStream_t s, const KernelEvents &ev) {
     constexpr bool S = MODE != kMass;
-    if (shape == 0) return launch_one<D, 1, 4, MODE, false>(p, s);
+    if (shape == 0) return launch_one<D, 1, 4, MODE, false>(p, s, ev);
     // the mass pass of larger requests: QG 4 (mass_rows_per_block rows), or
     // QG 2 (shape 3, d = 128: up to 256 rows per kv head)
     if constexpr (MODE == kMass) {
         if constexpr (D == 128) {
-            if (shape == 3) return launch_one<D, 2, 8, MODE, false>(p, s);
+            if (shape == 3) return launch_one<D, 2, 8, MODE, false>(p, s, ev);
         }
-        return launch_one<D, 4, D == 128 ? 8 : 4, MODE, false>(p, s);
+        return launch_one<D, 4, D == 128 ? 8 : 4, MODE, false>(p, s, ev);
     }
     else if constexpr (D == 128)
-        return shape == 2 ? launch_one<D, 2, 8, MODE, S>(p, s) : launch_one<D, 2, 8, MODE, false>(p, s);
+        return shape == 2 ? launch_one<D, 2, 8, MODE, S>(p, s, ev) : launch_one<D, 2, 8, MODE, false>(p, s, ev);
     else
-        return shape == 2 ? launch_one<D, 2, 4, MODE, S>(p, s) : launch_one<D, 2, 4, MODE, false>(p, s);
+        return shape == 2 ? launch_one<D, 2, 4, MODE, S>(p, s, ev) : launch_one<D, 2, 4, MODE, false>(p, s, ev);
 }
 
 template <int D>
-hipError_t launch_mode(const FwdParams &p, int mode, int shape, hipStream_t s) {
+hipError_t launch_mode(const FwdParams &p, int mode, int shape, hipStream_t s, const KernelEvents &ev) {
     switch (mode) {
-    case kAttn: return launch_shape<D, kAttn>(p, shape, s);
-    case kLse: return launch_shape<D, kLse>(p, shape, s);
-    default: return launch_shape<D, kMass>(p, shape, s);
+    case kAttn: return launch_shape<D, kAttn>(p, shape, s, ev);
+    case kLse: return launch_shape<D, kLse>(p, shape, s, ev);
+    default: return launch_shape<D, kMass>(p, shape, s, ev);
     }
 }
 
@@ -1364,8 +1366,8 @@ int mass_rows_per_block(int head_dim, int shape) {
     return head_dim == 128 ? (shape == 3 ? 256 : 512) : 256;
 }
 
-hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int shape, hipStream_t s) {
-    return head_dim == 64 ? launch_mode<64>(p, mode, shape, s) : launch_mode<128>(p, mode, shape, s);
+hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int shape, hipStream_t s, KernelEvents ev) {
+    return head_dim == 64 ? launch_mode<64>(p, mode, shape, s, ev) : launch_mode<128>(p, mode, shape, s, ev);
 }
 
 hipError_t launch_merge(const MergeParams &p, int head_dim, hipStream_t s) {

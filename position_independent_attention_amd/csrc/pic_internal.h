@@ -2,6 +2,7 @@
 // host-side launchers implemented in the kernel translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -132,6 +133,13 @@ struct FuseParams {
     int32_t n_sel;            // rows in k_new / v_new / sel_idx
 };
 
+// Kernel timing: when `start` is set, the main kernel of a launcher is
+// launched with hipExtLaunchKernelGGL, which stamps the two events with the
+// kernel's own start and end.
+struct KernelEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // Launchers (return the launch's hipError_t).
 // shape 0: 64 rows per workgroup; shape 1: 256 rows (d = 128) / 128 rows (d = 64);
 // shape 2: shape 1 skipping the tiles that no row of a workgroup sees
@@ -139,8 +147,9 @@ int fwd_rows_per_block(int head_dim, int shape);
 // rows per workgroup of the mass pass at shape >= 1: 4 row tiles per wave, or
 // 2 at shape 3 (d = 128 only)
 int mass_rows_per_block(int head_dim, int shape);
-hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int shape, hipStream_t s);
-hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t s);
+hipError_t launch_fwd(const FwdParams &p, int head_dim, int mode, int shape, hipStream_t s,
+                      KernelEvents ev = KernelEvents{});
+hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t s, KernelEvents ev = KernelEvents{});
 hipError_t launch_merge(const MergeParams &p, int head_dim, hipStream_t s);
 hipError_t launch_mass_reduce(const SelectParams &p, hipStream_t s);
 hipError_t launch_topk(const SelectParams &p, hipStream_t s);

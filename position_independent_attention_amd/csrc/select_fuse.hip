@@ -213,20 +213,21 @@ __global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
         if (p.sel_off[s] + i < p.max_sel) out[i] = -1;
 }
 
-// One workgroup per (fused block fb, request r), over every kv head: fresh
-// K rows are copied 16 bytes at a time; fresh V rows are staged in LDS with
-// 16-byte loads and written channel-major, 8 slots (16 bytes) per store.
-// Only the fresh slots of a partial last block are written.  The kv heads
-// go in passes of up to kFuseHeads, every load of a pass issued before its
-// first store, so a pass waits on one round trip.
-constexpr int kFuseHeads = 8;
+// One workgroup per (fused block fb, group of kFuseHeads kv heads, request r):
+// fresh K rows are copied 16 bytes at a time; fresh V rows are staged in LDS
+// with 16-byte loads and written channel-major, 8 slots (16 bytes) per store.
+// Only the fresh slots of a partial last block are written.  Every load of a
+// workgroup is issued before its first store, so it waits on one round trip;
+// the small workgroups (16 KB moved at d 128) keep several resident per CU.
+// The head-group-0 workgroups also rewrite the request's positions.
+constexpr int kFuseHeads = 2;
 
 template <int D>
 __global__ __launch_bounds__(256) void fuse_kernel(FuseParams p) {
     constexpr int CPR = D / 8;   // 16-byte chunks per row
     static_assert(kBlock * CPR <= 256, "one row chunk per thread");
     __shared__ __attribute__((aligned(16))) uint16_t s_v[kFuseHeads][kBlock][D + 8];
-    const int fb = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+    const int fb = blockIdx.x, g0 = blockIdx.y * kFuseHeads, r = blockIdx.z, tid = threadIdx.x;
     const int row0 = max(0, p.sel_req_off[r]);
     const int cnt = min(p.sel_req_off[r + 1], p.n_sel) - row0;
     const int kv_stride = p.max_blocks * kBlock;
@@ -234,59 +235,56 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseParams p) {
     kvl = kvl < 0 ? 0 : (kvl > kv_stride ? kv_stride : kvl);
     const int base = (kvl + kBlock - 1) / kBlock * kBlock;
     int32_t *pis = p.kv_pos + (size_t)r * kv_stride;
-    if (fb == 0) {
+    if (fb == 0 && g0 == 0) {
         for (int j = kvl + tid; j < base; j += 256) pis[j] = -1;
     }
     const int n_here = min(kBlock, cnt - kBlock * fb);
-    if (n_here <= 0) return;
+    if (n_here <= 0 || g0 >= p.hkv) return;
     const int bidx = base / kBlock + fb;
     if (bidx >= p.max_blocks) return;
     const int blk = p.block_table[(size_t)r * p.max_blocks + bidx];
     if (blk < 0 || blk >= p.num_blocks) return;
     const int rowb = row0 + kBlock * fb;
+    const int ng = min(kFuseHeads, p.hkv - g0);
     // this thread's chunk: slot sl, 16-byte column c
     const int sl = tid / CPR, c = tid % CPR;
     const bool has = tid < kBlock * CPR;
     const bool fresh = has && sl < n_here;
 
-    for (int g0 = 0; g0 < p.hkv; g0 += kFuseHeads) {
-        const int ng = min(kFuseHeads, p.hkv - g0);
-        u32x4 kc[kFuseHeads], vc[kFuseHeads];
+    u32x4 kc[kFuseHeads], vc[kFuseHeads];
 #pragma unroll
-        for (int gi = 0; gi < kFuseHeads; ++gi) {
-            kc[gi] = vc[gi] = u32x4{0u, 0u, 0u, 0u};
-            if (gi < ng && fresh) {
-                const size_t src = ((size_t)(rowb + sl) * p.hkv + g0 + gi) * D + 8 * c;
-                kc[gi] = *reinterpret_cast<const u32x4 *>(p.k_new + src);
-                vc[gi] = *reinterpret_cast<const u32x4 *>(p.v_new + src);
-            }
+    for (int gi = 0; gi < kFuseHeads; ++gi) {
+        kc[gi] = vc[gi] = u32x4{0u, 0u, 0u, 0u};
+        if (gi < ng && fresh) {
+            const size_t src = ((size_t)(rowb + sl) * p.hkv + g0 + gi) * D + 8 * c;
+            kc[gi] = *reinterpret_cast<const u32x4 *>(p.k_new + src);
+            vc[gi] = *reinterpret_cast<const u32x4 *>(p.v_new + src);
         }
+    }
 #pragma unroll
-        for (int gi = 0; gi < kFuseHeads; ++gi) {
-            if (gi < ng && fresh)   // K rows: token-major in the pool
-                *reinterpret_cast<u32x4 *>(p.k_pool + (((size_t)blk * p.hkv + g0 + gi) * kBlock + sl) * D + 8 * c) =
-                    kc[gi];
-            if (gi < ng && has) *reinterpret_cast<u32x4 *>(&s_v[gi][sl][8 * c]) = vc[gi];
-        }
-        __syncthreads();
-        // V: channel-major, thread -> (head, channel d, slots 8h .. 8h+7)
-        for (int t = tid; t < ng * 2 * D; t += 256) {
-            const int gi = t / (2 * D), d = (t >> 1) % D, h = t & 1;
-            uint16_t *dst = p.v_pool + (((size_t)blk * p.hkv + g0 + gi) * D + d) * kBlock + 8 * h;
-            if (8 * h + 8 <= n_here) {
-                u32x4 w;
+    for (int gi = 0; gi < kFuseHeads; ++gi) {
+        if (gi < ng && fresh)   // K rows: token-major in the pool
+            *reinterpret_cast<u32x4 *>(p.k_pool + (((size_t)blk * p.hkv + g0 + gi) * kBlock + sl) * D + 8 * c) =
+                kc[gi];
+        if (gi < ng && has) *reinterpret_cast<u32x4 *>(&s_v[gi][sl][8 * c]) = vc[gi];
+    }
+    __syncthreads();
+    // V: channel-major, thread -> (head, channel d, slots 8h .. 8h+7)
+    for (int t = tid; t < ng * 2 * D; t += 256) {
+        const int gi = t / (2 * D), d = (t >> 1) % D, h = t & 1;
+        uint16_t *dst = p.v_pool + (((size_t)blk * p.hkv + g0 + gi) * D + d) * kBlock + 8 * h;
+        if (8 * h + 8 <= n_here) {
+            u32x4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = (uint32_t)s_v[gi][8 * h + 2 * e][d] | ((uint32_t)s_v[gi][8 * h + 2 * e + 1][d] << 16);
-                *reinterpret_cast<u32x4 *>(dst) = w;
-            } else {
-                for (int i = 0; i < 8 && 8 * h + i < n_here; ++i) dst[i] = s_v[gi][8 * h + i][d];
-            }
+            for (int e = 0; e < 4; ++e)
+                w[e] = (uint32_t)s_v[gi][8 * h + 2 * e][d] | ((uint32_t)s_v[gi][8 * h + 2 * e + 1][d] << 16);
+            *reinterpret_cast<u32x4 *>(dst) = w;
+        } else {
+            for (int i = 0; i < 8 && 8 * h + i < n_here; ++i) dst[i] = s_v[gi][8 * h + i][d];
         }
-        __syncthreads();
     }
     // positions: fresh slot takes the stale slot's pi, the stale slot is masked
-    if (tid < n_here) {
+    if (g0 == 0 && tid < n_here) {
         const int i = kBlock * fb + tid;
         const int sel = p.sel_idx[row0 + i];
         const int slot = base + i;
@@ -383,7 +381,7 @@ hipError_t launch_topk(const SelectParams &p, hipStream_t s) {
 hipError_t launch_fuse(const FuseParams &p, int head_dim, hipStream_t s) {
     if (p.batch <= 0) return hipSuccess;
     const int nfb = p.max_rows > 0 ? (p.max_rows + kBlock - 1) / kBlock : 1;
-    const dim3 grid(nfb, p.batch);
+    const dim3 grid(nfb, (p.hkv + kFuseHeads - 1) / kFuseHeads, p.batch);
     if (head_dim == 64)
         hipLaunchKernelGGL(fuse_kernel<64>, grid, dim3(256), 0, s, p);
     else

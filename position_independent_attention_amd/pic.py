@@ -105,6 +105,10 @@ def lib() -> C.CDLL:
         h.pic_block_map.restype = C.c_int
         h.kv_fuse_scatter.argtypes = [_vp, P(PicKvPool), P(PicReqTable), _vp, _vp, _vp, _vp, _i32, _i32, _vp]
         h.kv_fuse_scatter.restype = C.c_int
+        h.pic_timing_start.argtypes = [_vp, _i32]
+        h.pic_timing_start.restype = C.c_int
+        h.pic_timing_stop.argtypes = [_vp, _vp, _vp, _i32, P(_i32)]
+        h.pic_timing_stop.restype = C.c_int
         _lib = h
     return _lib
 
@@ -222,6 +226,21 @@ def pic_workspace_bytes(ctx: Context, op: int, req: PicReqTable, total_q: int, m
     _check(ctx, lib().pic_workspace_bytes(ctx.handle, op, C.byref(req), total_q, max_q_len, C.byref(n)),
            "pic_workspace_bytes")
     return int(n.value)
+
+
+def pic_timing_start(ctx: Context, capacity: int):
+    _check(ctx, lib().pic_timing_start(ctx.handle, int(capacity)), "pic_timing_start")
+
+
+def pic_timing_stop(ctx: Context, cap: int):
+    """-> (ms, ops): the recorded kernel intervals in call order."""
+    ms = np.zeros(max(1, cap), np.float32)
+    ops = np.zeros(max(1, cap), np.int32)
+    n = _i32(0)
+    _check(ctx, lib().pic_timing_stop(ctx.handle, ms.ctypes.data, ops.ctypes.data, int(cap), C.byref(n)),
+           "pic_timing_stop")
+    k = min(int(n.value), cap)
+    return ms[:k].copy(), ops[:k].copy()
 
 
 def pic_select_offsets(span_len: np.ndarray, ratio: float) -> np.ndarray:

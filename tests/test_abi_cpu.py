@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     h = pic.lib()
     for n in names:
         assert hasattr(h, n), n
@@ -76,6 +76,9 @@ def test_entry_points_reject_null_context():
     assert h.qc_anchor_select(None, C.byref(pool), C.byref(req), C.byref(sp), 0, None, None, None, 0, None) == 1
     n = C.c_size_t()
     assert h.pic_workspace_bytes(None, 0, C.byref(req), 0, 0, C.byref(n)) == 1
+    cnt = C.c_int32()
+    assert h.pic_timing_start(None, 8) == 1
+    assert h.pic_timing_stop(None, None, None, 0, C.byref(cnt)) == 1
 
 
 def test_peaks_library_exports_its_header():
