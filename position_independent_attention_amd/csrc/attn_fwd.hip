@@ -460,20 +460,37 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     const int sp = lid % p.num_splits;
     const int r = lid / p.num_splits;
 
+    const int kv_stride = p.max_blocks * kBlock;
+    const int kv_cap = min(kv_stride, p.max_kv_len);
+    const int key_begin = sp * p.split_len;
+    const int32_t *bt = p.block_table + (size_t)r * p.max_blocks;
+    const int32_t *pis = p.kv_pos + (size_t)r * kv_stride;
+    const int tid = threadIdx.x;
+
+    // ---- requests that need nothing loaded go first: block ids and
+    // positions of tiles 0 and 1 and of the masking pre-pass, at indices
+    // clamped by the split's host-side bound (all inside the request's rows),
+    // in the same round trip as kv_len; the true range is applied where the
+    // values are used.  Tile 0's K / V / table rows follow them, and the
+    // queries' rows follow the queries' positions, so the prologue waits on
+    // about two round trips.
+    const int key_end_h = min(kv_cap, key_begin + p.split_len);
+    Meta<D, WAVES> m1, m2;
+    Data<D, WAVES> dnext;
+    if (key_end_h > key_begin) {
+        meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end_h, tid);
+        meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end_h, tid);
+    }
+    const FbPre fb = fb_preload<GG::NT>(bt, pis, key_begin, key_end_h, tid);
+
     const int q0 = p.q_start[r];
     const int nq = p.q_start[r + 1] - q0;
     const int nrows = nq * p.group;
     if (rb * BM >= nrows) return;
-    const int kv_stride = p.max_blocks * kBlock;
-    const int kv_cap = min(kv_stride, p.max_kv_len);
     int kvl = p.kv_len[r];
     kvl = kvl < 0 ? 0 : (kvl > kv_cap ? kv_cap : kvl);
-    const int key_begin = sp * p.split_len;
     const int key_end = min(kvl, key_begin + p.split_len);
-    const int32_t *bt = p.block_table + (size_t)r * p.max_blocks;
-    const int32_t *pis = p.kv_pos + (size_t)r * kv_stride;
 
-    const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int lc = lane & 15, lg = lane >> 4;
     if (tid == 0) {
@@ -484,19 +501,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     }
     if constexpr (SKIP)
         for (int w = tid; w < kNeedWords; w += GG::NT) s_need[w] = 0u;
-
-    // ---- requests that need nothing from the rows go first: block ids and
-    // positions of tiles 0 and 1 and of the masking pre-pass.  Tile
-    // 0's K / V / table rows follow the rows' positions, and the queries'
-    // rows follow those, so the prologue waits on about two round trips.
     const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
-    Meta<D, WAVES> m1, m2;
-    Data<D, WAVES> dnext;
-    if (ntiles > 0) {
-        meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end, tid);
-        meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
-    }
-    const FbPre fb = fb_preload<GG::NT>(bt, pis, key_begin, key_end, tid);
 
     // ---- this lane's query columns: load, rotate at q_pos, keep as B operands
     u32x4 qop[QG][GG::NC];
@@ -971,20 +976,32 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
     const int sp = lid % p.num_splits;
     const int r = lid / p.num_splits;
 
+    const int kv_stride = p.max_blocks * kBlock;
+    const int kv_cap = min(kv_stride, p.max_kv_len);
+    const int key_begin = sp * p.split_len;
+    const int32_t *bt = p.block_table + (size_t)r * p.max_blocks;
+    const int32_t *pis = p.kv_pos + (size_t)r * kv_stride;
+    const int tid = threadIdx.x;
+
+    // ---- requests that need nothing loaded first, clamped by the split's
+    // host-side bound (as in fwd_kernel)
+    const int key_end_h = min(kv_cap, key_begin + p.split_len);
+    Meta<D, WAVES> m1, m2;
+    Data<D, WAVES> dnext;
+    if (key_end_h > key_begin) {
+        meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end_h, tid);
+        meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end_h, tid);
+    }
+    const FbPre fb = fb_preload<GG::NT>(bt, pis, key_begin, key_end_h, tid);
+
     const int q0 = p.q_start[r];
     const int nq = p.q_start[r + 1] - q0;
     const int nrows = nq * p.group;
     if (rb * BM >= nrows) return;
-    const int kv_stride = p.max_blocks * kBlock;
-    const int kv_cap = min(kv_stride, p.max_kv_len);
     int kvl = p.kv_len[r];
     kvl = kvl < 0 ? 0 : (kvl > kv_cap ? kv_cap : kvl);
-    const int key_begin = sp * p.split_len;
     const int key_end = min(kvl, key_begin + p.split_len);
-    const int32_t *bt = p.block_table + (size_t)r * p.max_blocks;
-    const int32_t *pis = p.kv_pos + (size_t)r * kv_stride;
 
-    const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int lc = lane & 15, lg = lane >> 4;
     if (tid == 0) {
@@ -992,16 +1009,7 @@ __global__ __launch_bounds__(64 * WAVES) void mass_kernel(FwdParams p) {
         s_firstbad = 0x7fffffff;
     }
     const int row0 = rb * BM + wave * 16 * QG;   // first row of this wave
-
-    // ---- requests that need nothing from the rows first (as in fwd_kernel)
     const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
-    Meta<D, WAVES> m1, m2;
-    Data<D, WAVES> dnext;
-    if (ntiles > 0) {
-        meta_load<D, WAVES>(m1, bt, pis, key_begin, key_end, tid);
-        meta_load<D, WAVES>(m2, bt, pis, key_begin + kTileN, key_end, tid);
-    }
-    const FbPre fb = fb_preload<GG::NT>(bt, pis, key_begin, key_end, tid);
 
     // ---- A operands: query row lc of each row tile, rotated at its q_pos
     u32x4 qop[QG][GG::NC];
