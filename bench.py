@@ -89,7 +89,8 @@ ANCHOR_RATIO = 0.05   # anchor fraction per span (the pages say only "a small fr
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 MAX_CPU_WORKERS = 16  # the CPU share of one GPU on the GPU hosts
-LINES = ["step", "shared_serving", "selection_64q", "decode", "recompute", "anchor", "ablation", "hashing"]
+LINES = ["step", "select_lse_null", "llama_layer", "shared_serving", "selection_64q", "decode", "recompute", "anchor",
+         "ablation", "hashing"]
 
 
 def log(*a):
@@ -724,6 +725,50 @@ def main():
                        "data": "synthetic", "config": {"workload": "long_context_qc_fusion"}})
     if peaks:
         result["measured_peaks"] = peaks
+
+    if "select_lse_null" in only:
+        # qc_score_select with no caller LSE: the K-only LSE pass (split
+        # partials + merge) runs first, then the mass pass, the column reduction
+        # and the top-k; both passes read K only
+        state.copy_(state0)
+        dc.max_kv_len = kv0
+        msn, kmn = time_calls(lambda: pic.qc_score_select(ctx, dc, None, nsel, sel, None, ws=ws, stream=stream),
+                              reps=args.steps, warm=args.warmup, kctx=ctx)
+        qk2 = 2 * pairs * w.num_q_heads * 2 * w.head_dim
+        result["select_lse_null"] = {
+            "workload": "qc_score_select of the long-context step's 256 query tokens with lse = NULL "
+                        "(the selection computes its own LSE), top 15% per span",
+            "ms_per_call": round(msn, 5), "mass_kernel_ms": round(kmn, 5),
+            "roofline": roof("mfma", qk2 / (msn / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
+                             algorithmic_flops=qk2, avg_ms=round(msn, 5),
+                             note="QK^T twice (the LSE pass and the mass pass) over the whole call; "
+                                  "the exp count is the same twice, 2 x 269.5 M")}
+
+    if "llama_layer" in only:
+        # One Llama-3-8B-like layer: 64 query tokens over a 64-token private
+        # prefix and eight reused 512-token spans (4,224 slots), 32 q / 8 kv heads
+        wl = W.llama_layer()
+        dl = pic.to_device(wl, dev)
+        ol = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.int16, device=dev)
+        ll = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device=dev)
+        wsl = torch.empty(max(1, pic.pic_workspace_bytes(ctx, pic.PIC_OP_PREFILL, dl.req(), wl.total_q,
+                                                         wl.max_q_len)), dtype=torch.uint8, device=dev)
+        ml, kl = time_calls(lambda: pic.pic_attn_prefill(ctx, dl, ol, ll, ws=wsl, stream=stream), reps=50, warm=5,
+                            kctx=ctx)
+        tl, pl = attended_tokens(wl), visible_pairs(wl)
+        fl = pl * wl.num_q_heads * 4 * wl.head_dim
+        kvb = tl * wl.num_kv_heads * wl.head_dim * 2 * 2
+        result["llama_layer"] = {
+            "workload": f"1 request, {tl} KV slots (64-token private prefix + 8 x 512 reused spans) + "
+                        f"{wl.total_q} query tokens, 32 q / 8 kv heads, d 128: pic_attn_prefill with lse",
+            "ms_per_call": round(ml, 5), "kernel_ms": round(kl, 5),
+            "attended_kv_tokens_per_s": round(tl / (ml / 1e3), 1),
+            "roofline": roof("mfma", fl / (kl / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
+                             algorithmic_flops=fl, avg_ms=round(kl, 5), kernel="the prefill kernel",
+                             note="near the MFMA/HBM ridge and launch-bound at one request"),
+            "hbm": roof("hbm", kvb / (kl / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s", mp_hbm, algorithmic_bytes=kvb,
+                        avg_ms=round(kl, 5))}
+        del dl, ol, ll, wsl
 
     ablation = None
     if "ablation" in only:

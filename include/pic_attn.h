@@ -162,7 +162,10 @@ const char *pic_ctx_last_error(const pic_ctx *ctx);
  * the split merge, the decode kernel without its merge, the selection's mass
  * pass without the column reduction and the top-k) with an event pair that
  * HIP stamps at that kernel's own start and end (hipExtLaunchKernelGGL),
- * until capacity intervals are held; later calls run untimed.  pic_timing_stop waits for the last recorded event,
+ * until capacity intervals are held; later calls run untimed.  A call that
+ * launches no such kernel (an empty batch, no query tokens, an error)
+ * records nothing.  The stamps include the kernel's dispatch, a few
+ * microseconds that a profiler's kernel trace leaves out.  pic_timing_stop waits for the last recorded event,
  * writes the first min(cap, count) intervals in call order (ms: elapsed
  * milliseconds; ops: the pic_op of the call, either array may be NULL),
  * sets *count to the number of intervals recorded, destroys the events and

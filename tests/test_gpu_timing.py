@@ -63,9 +63,17 @@ def test_timing_intervals_follow_the_calls():
     # outputs of the last (untimed) round are those of the runs without timing
     for (_, _, _, o), r in zip(calls, ref):
         assert torch.equal(o, r)
-    # timing off again: calls record nothing and a new session starts empty
+    # timing off again: calls record nothing and a new session starts empty;
+    # a call that launches no kernel (no query tokens) records nothing either
     calls[0][2]()
     pic.pic_timing_start(ctx, 2)
+    dc = pic.to_device(w, H.DEV)
+    empty = pic.DeviceCache(dc.pool_k, dc.pool_v, dc.block_table, dc.kv_len, dc.kv_pos, dc.max_kv_len, q=dc.q,
+                            q_start=torch.zeros(2, dtype=torch.int32, device=H.DEV), q_pos=dc.q_pos, total_q=0,
+                            max_q_len=0)
+    o0 = torch.empty((1, w.num_q_heads, w.head_dim), dtype=torch.int16, device=H.DEV)
+    pic.pic_attn_prefill(ctx, empty, o0)
+    torch.cuda.synchronize()
     ms, ops = pic.pic_timing_stop(ctx, 2)
     assert len(ms) == 0
     ctx.close()
