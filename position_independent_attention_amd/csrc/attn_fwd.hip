@@ -851,12 +851,14 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
                     p.mass_part[(((size_t)r * p.hkv + g) * p.row_blocks + rb) * p.mass_stride + j] = tot;
             }
         }
-        // R4: QK(next tile, half 0) || request the tile after it
+        // R4: request the tile after the next one || QK(next tile, half 0).
+        // The requests go first: they fill the wait for the K operands that
+        // every wave reads from LDS right after the barrier.
         if constexpr (MORE) {
-            qk_half(cur ^ 1, 0, sA);
             data_load<D, WAVES, true>(p, dnext, m2, g, SKIP ? key_begin + n2 * kTileN : tile + 2 * kTileN, key_end, tid,
                                 kV);
             meta_load<D, WAVES>(m2, bt, pis, SKIP ? key_begin + n3 * kTileN : tile + 3 * kTileN, key_end, tid);
+            qk_half(cur ^ 1, 0, sA);
         }
         (void)n1;
     };
