@@ -45,6 +45,7 @@
 //   touched by VALU.
 #include "pic_internal.h"
 
+#include <cfloat>
 #include <type_traits>
 
 namespace pic {
@@ -386,10 +387,11 @@ __device__ __forceinline__ int first_bad_key(const FwdParams &p, const int32_t *
 // Rotate and write one tile into an LDS buffer.  With s_bias, also writes
 // each key's score bias (0 if usable, -inf if not); with K rows of unusable
 // keys loaded as zeros their scores are then exactly -inf without a
-// per-score test.
+// per-score test.  With s_mask, also each key's weight in the row sums as a
+// bf16 1 (usable) or 0.
 template <int D, int WAVES, bool ROT>
 __device__ __forceinline__ void data_store(Data<D, WAVES> &dt, uint16_t *Ks, uint16_t *Vs, int32_t *s_pi, int tid,
-                                           bool need_v, float *s_bias = nullptr) {
+                                           bool need_v, float *s_bias = nullptr, uint16_t *s_mask = nullptr) {
     using GG = Geo<D, WAVES>;
 #pragma unroll
     for (int u = 0; u < GG::KTASK; ++u) {
@@ -404,6 +406,7 @@ __device__ __forceinline__ void data_store(Data<D, WAVES> &dt, uint16_t *Ks, uin
         // masked-path visibility is one compare: unusable keys get INT_MAX
         if (pc == 0) s_pi[kk] = pi >= 0 ? pi : 0x7fffffff;
         if (s_bias && pc == 0) s_bias[kk] = pi >= 0 ? 0.f : -INFINITY;
+        if (s_mask && pc == 0) s_mask[kk] = pi >= 0 ? 0x3f80 : 0;
     }
     if (need_v) {
         int half, dd;
@@ -443,6 +446,11 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(16))) int32_t s_pi[2 * kTileN];
     // score bias of each staged key: 0, or -inf for an unusable key
     __shared__ __attribute__((aligned(16))) float s_bias[2 * kTileN];
+    // weight of each staged key in the row sums: bf16 1, or 0 if unusable
+    __shared__ __attribute__((aligned(16))) uint16_t s_maskb[2 * kTileN];
+    // each lane's QK accumulator start per row tile, -u (4 equal values):
+    // read by the lane itself before every QK, rewritten when u moves
+    __shared__ __attribute__((aligned(16))) f32x4 s_negmu[MODE == kMass ? 1 : WAVES * QG * 64];
     __shared__ float s_red[MODE == kMass ? 2 * WAVES * kTileN : 1];
     __shared__ int32_t s_minpos, s_firstbad, s_lastbad, s_maxpos;
     // bit t: tile t holds a key that some row of the workgroup sees
@@ -503,7 +511,10 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         for (int w = tid; w < kNeedWords; w += GG::NT) s_need[w] = 0u;
     const int ntiles = key_end > key_begin ? (key_end - key_begin + kTileN - 1) / kTileN : 0;
 
-    // ---- this lane's query columns: load, rotate at q_pos, keep as B operands
+    // ---- this lane's query columns: load, rotate at q_pos, scale by
+    // log2(e)/sqrt(d) in fp32, round to bf16 and keep as B operands: the QK
+    // MFMAs then give the scores in log2 units
+    const float sc = p.scale_log2;
     u32x4 qop[QG][GG::NC];
     int qpos[QG], qt[QG], qh[QG];
     bool qvalid[QG];
@@ -547,23 +558,21 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
                 const float *cr = p.cos_tab + (size_t)pos * GG::HALF + i0;
                 const float *sr = p.sin_tab + (size_t)pos * GG::HALF + i0;
                 rope8(lo, hi, *reinterpret_cast<const f32x4 *>(cr), *reinterpret_cast<const f32x4 *>(cr + 4),
-                      *reinterpret_cast<const f32x4 *>(sr), *reinterpret_cast<const f32x4 *>(sr + 4));
+                      *reinterpret_cast<const f32x4 *>(sr), *reinterpret_cast<const f32x4 *>(sr + 4), sc);
                 qop[qg][c] = lo;
                 qop[qg][c + GG::NC / 2] = hi;
             }
         }
     }
 
-    // Running max in log2 units.  Starting from a finite -1e30 (instead of
-    // -inf) keeps exp2(s*scale - m) well defined without a select: the first
-    // visible score always triggers a rescale, and fully masked columns give
-    // exp2(-inf) = 0.
+    // Running max in log2 units: a finite -1e30 until the column has seen a
+    // usable key.
     float m_run[QG], lse2[QG];
     f32x4 acc[kV ? QG : 1][kV ? D / 16 : 1];
-    // Row sums of P on the MFMA pipe: A = 16 x 32 with ones in row 0, so row 0
-    // of acc_l[qg] accumulates sum_k P^T[k][col] (lanes of group 0, element 0).
+    // Row sums of P on the MFMA pipe: A = 16 x 32 whose every row holds the
+    // keys' weights (1, or 0 for an unusable key), so each row of acc_l[qg]
+    // accumulates sum_k w_k P^T[k][col].
     f32x4 acc_l[MODE == kMass ? 1 : QG];
-    const u32x4 ones_a = lc == 0 ? u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u} : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
         m_run[qg] = -1e30f;
@@ -643,13 +652,26 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         cs_load<D, WAVES, ROT>(p, dnext, tid);
     }
     if (SKIP ? it0 < ntiles : ntiles > 0) {
-        data_store<D, WAVES, ROT>(dnext, Ks, Vs, s_pi, tid, kV, s_bias);
+        data_store<D, WAVES, ROT>(dnext, Ks, Vs, s_pi, tid, kV, s_bias, s_maskb);
         __syncthreads();
     }
-    const float sc = p.scale_log2;
-    float m_ref[QG];                    // reference max of the next P half
+    // The softmax reference of each column: m_ref, the max the accumulators
+    // are in (-1e30 until a usable key is seen).  The QK accumulators start
+    // at -u (negmu), u = m_ref once set, else 0, so every score arrives as
+    // s' = s - u and P = exp2(s') needs no VALU op before the exp.  An
+    // unusable key (K row zero) then scores exactly -u: its P is finite while
+    // -u <= the slack and it is weighted 0 in the row sums (V row zero);
+    // a larger -u trips the reference check, whose rare path adds the key
+    // bias (-inf) before forming P.  thr: the check's threshold on the
+    // half's lane max, the slack once set, else -FLT_MAX (any visible key).
+    float m_ref[QG], thr[QG];
+    f32x4 *negmu = s_negmu + (MODE == kMass ? 0 : wave * QG * 64 + lane);   // row tile qg at [64 qg]
 #pragma unroll
-    for (int qg = 0; qg < QG; ++qg) m_ref[qg] = m_run[qg];
+    for (int qg = 0; qg < QG; ++qg) {
+        m_ref[qg] = m_run[qg];
+        thr[qg] = -FLT_MAX;
+        if constexpr (MODE != kMass) negmu[64 * qg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // ---- software pipeline over 32-key halves.  Per tile:
     //   R1  QK(half 1)            || softmax(half 0)
@@ -657,19 +679,26 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     //   R3  PV(half 1)            || rotate + stage the next tile
     //   --  barrier
     //   R4  QK(next tile, half 0)
-    // Every softmax uses the reference max the accumulators are in (so the
-    // scores and the max reduction are independent of the MFMAs in flight);
-    // when a half's max passes it by more than 2^8 (rare after the first
-    // keys), the reference moves, the accumulators follow before that half's
-    // PV and its P is formed again.
-    // buf: LDS buffer of the tile.  The accumulators start at the keys'
-    // score bias (-inf cuts an unusable key; its K row is zero).
+    // Every softmax uses the reference the accumulators are in; when a
+    // half's max passes it by more than 2^8 (rare after the first keys), the
+    // reference moves, the accumulators follow before that half's PV, and the
+    // half's scores (and those of the other half in flight) are shifted and
+    // its P is formed again.
+    // buf: LDS buffer of the tile.  The accumulators start at -u of their
+    // column (attention, LSE) or at the keys' score bias (mass: -inf cuts an
+    // unusable key, whose K row is zero).
     auto qk_half = [&](int buf, int kh, f32x4 (&sacc)[QG][2]) {
         const uint16_t *Kb = Ks + buf * GG::KBUF;
         // sacc[.][T][i] holds key 32 kh + 8 lg + 4 T + i
-        const float *bb = s_bias + buf * kTileN + 32 * kh + 8 * lg;
-        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bb);
-        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(bb + 4);
+        f32x4 b0, b1, nm[QG];
+        if constexpr (MODE == kMass) {
+            const float *bb = s_bias + buf * kTileN + 32 * kh + 8 * lg;
+            b0 = *reinterpret_cast<const f32x4 *>(bb);
+            b1 = *reinterpret_cast<const f32x4 *>(bb + 4);
+        } else {
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) nm[qg] = negmu[64 * qg];
+        }
         // d-chunk outermost: 2*QG independent accumulators separate the
         // dependent MFMAs of one accumulator chain
         // rows 32*kh + 16*T + lc (T = 0, 1), chunk 4c + lg: the XOR stays
@@ -682,13 +711,19 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
             const u32x4 a1 = *reinterpret_cast<const u32x4 *>(k0 + 16 * 8);
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) {
-                sacc[qg][0] = mfma16(a0, qop[qg][c], c == 0 ? b0 : sacc[qg][0]);
-                sacc[qg][1] = mfma16(a1, qop[qg][c], c == 0 ? b1 : sacc[qg][1]);
+                if constexpr (MODE == kMass) {
+                    sacc[qg][0] = mfma16(a0, qop[qg][c], c == 0 ? b0 : sacc[qg][0]);
+                    sacc[qg][1] = mfma16(a1, qop[qg][c], c == 0 ? b1 : sacc[qg][1]);
+                } else {
+                    sacc[qg][0] = mfma16(a0, qop[qg][c], c == 0 ? nm[qg] : sacc[qg][0]);
+                    sacc[qg][1] = mfma16(a1, qop[qg][c], c == 0 ? nm[qg] : sacc[qg][1]);
+                }
             }
         }
     };
-    // Scores of one half -> masked, scaled exp2 -> bf16 P^T operands (attn /
-    // lse) or column sums (mass).  Returns the scaled column maxima in mx.
+    // Scores of one half (log2 units) -> masked exp2 -> bf16 P^T operands
+    // (attn / lse) or column sums (mass).  Returns the lane maxima of the
+    // shifted scores in mx.
     auto softmax_half = [&](auto full_c, const f32x4 (&sacc)[QG][2], const int32_t *pib, int kh,
                             u32x4 (&pb)[QG], float (&mx)[QG], float (&cs)[16]) {
         constexpr bool FULL = decltype(full_c)::value;
@@ -713,24 +748,24 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
             }
             if constexpr (MODE == kMass) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) cs[kh * 8 + e] += fast_exp2(fmaf(s[e], sc, -lse2[qg]));
+                for (int e = 0; e < 8; ++e) cs[kh * 8 + e] += fast_exp2(s[e] - lse2[qg]);
             } else {
-                const float mu = m_ref[qg];
                 u32x4 pq;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    pq[e] = pack2(fast_exp2(fmaf(s[2 * e], sc, -mu)), fast_exp2(fmaf(s[2 * e + 1], sc, -mu)));
+                for (int e = 0; e < 4; ++e) pq[e] = pack2(fast_exp2(s[2 * e]), fast_exp2(s[2 * e + 1]));
                 pb[qg] = pq;
-                // lane-local maximum of the raw scores; the column maximum
-                // is only formed when some lane passes the reference
+                // lane-local maximum of the shifted scores; the column
+                // maximum is only formed when some lane passes the check
                 mx[qg] = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
             }
         }
     };
-    auto pv_half = [&](const uint16_t *Vb, int kh, const u32x4 (&pb)[QG]) {
+    auto pv_half = [&](const uint16_t *Vb, const uint16_t *mb, int kh, const u32x4 (&pb)[QG]) {
         if constexpr (MODE != kMass) {
+            // the weights of keys 32 kh + 8 lg + e: the A operand of every row
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(mb + 32 * kh + 8 * lg);
 #pragma unroll
-            for (int qg = 0; qg < QG; ++qg) acc_l[qg] = mfma16(ones_a, pb[qg], acc_l[qg]);
+            for (int qg = 0; qg < QG; ++qg) acc_l[qg] = mfma16(w, pb[qg], acc_l[qg]);
         }
         if constexpr (kV) {
 #pragma unroll
@@ -752,27 +787,65 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
             for (int dt = 0; dt < D / 16; ++dt) acc[qg][dt] *= alpha;
         }
     };
-    // After a half whose lane-local raw maxima are mx: only when some lane
-    // passed the reference by more than the slack (wave-uniform branch, rare
-    // once the first keys are seen) are the column maxima formed; columns
-    // whose maximum passed it move their reference there, the accumulators
-    // follow at once (nothing of this half is in them yet) and the half's P
-    // is formed again against the new reference.  The common path is one
-    // compare per column and no branch target inside the MFMA / VALU regions.
-    auto settle = [&](auto full_c, const f32x4 (&sacc)[QG][2], const int32_t *pib, int kh, u32x4 (&pb)[QG],
-                      const float (&mx)[QG], float (&cs)[16]) {
+    // After a half whose lane maxima of the shifted scores are mx: only when
+    // some lane passes thr (wave-uniform branch, rare once the first keys are
+    // seen) are the column maxima formed.  In a mask-free tile the scores
+    // first take the key bias, so that unusable keys count nowhere.  Columns
+    // whose maximum passed move their reference there; the accumulators
+    // follow at once (nothing of this half is in them yet), this half's
+    // scores and, with SHIFT_OTHER, those of the other half already issued
+    // are shifted to the new reference, and the half's P is formed again.
+    // The common path is one compare per column and no branch target inside
+    // the MFMA / VALU regions.
+    auto settle = [&](auto full_c, auto shift_other_c, f32x4 (&sacc)[QG][2], f32x4 (&other)[QG][2],
+                      const int32_t *pib, const float *bb, int kh, u32x4 (&pb)[QG], const float (&mx)[QG],
+                      float (&cs)[16]) {
+        constexpr bool FULL = decltype(full_c)::value;
         bool need = false;
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) need = need || mx[qg] * sc > m_ref[qg] + kRescaleSlack;
-        if (__any(need)) {
-            float mx2[QG];
+        for (int qg = 0; qg < QG; ++qg) need = need || mx[qg] > thr[qg];
+        if (__builtin_expect(__any(need), 0)) {
+            float lm[QG];
+            if constexpr (FULL) {
+                const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bb + 32 * kh + 8 * lg);
+                const f32x4 b1 = *reinterpret_cast<const f32x4 *>(bb + 32 * kh + 8 * lg + 4);
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg) {
+                    sacc[qg][0] += b0;
+                    sacc[qg][1] += b1;
+                    float m = sacc[qg][0][0];
+#pragma unroll
+                    for (int e = 1; e < 8; ++e) m = fmaxf(m, sacc[qg][e >> 2][e & 3]);
+                    lm[qg] = m;
+                }
+            } else {
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg) lm[qg] = mx[qg];
+            }
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) {
-                const float cm = col_max(mx[qg]) * sc;
-                const float m_new = cm > m_ref[qg] + kRescaleSlack ? cm : m_ref[qg];
+                const float cm = col_max(lm[qg]);
+                const bool was = thr[qg] > 0.f;
+                const bool move = cm > thr[qg];
+                const float u = was ? m_ref[qg] : 0.f;
+                const float m_new = move ? u + cm : m_ref[qg];
+                // before a column has seen a usable key its accumulators are
+                // zero and exp2(-1e30 - m_new) = 0 keeps them so
                 rescale(qg, m_ref[qg], m_new);
+                const bool now = was || move;
+                const float un = now ? m_new : 0.f;
+                const float delta = un - u;
                 m_ref[qg] = m_new;
+                thr[qg] = now ? kRescaleSlack : -FLT_MAX;
+                negmu[64 * qg] = f32x4{-un, -un, -un, -un};
+                sacc[qg][0] -= delta;
+                sacc[qg][1] -= delta;
+                if constexpr (decltype(shift_other_c)::value) {
+                    other[qg][0] -= delta;
+                    other[qg][1] -= delta;
+                }
             }
+            float mx2[QG];
             softmax_half(full_c, sacc, pib, kh, pb, mx2, cs);
         }
     };
@@ -795,6 +868,8 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         const int tile = key_begin + it * kTileN;
         const uint16_t *Vc = Vs + (kV ? cur * GG::VBUF : 0);
         const int32_t *pc_ = s_pi + cur * kTileN;
+        const float *bc = s_bias + cur * kTileN;
+        const uint16_t *mc = s_maskb + cur * kTileN;
         u32x4 pb0[QG], pb1[QG];
         float mx0[QG], mx1[QG];
         float cs[16];   // kMass: column sums of this lane's 16 keys
@@ -805,19 +880,19 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         qk_half(cur, 1, sB);
         softmax_half(full_c, sA, pc_, 0, pb0, mx0, cs);
         interleave_hint<2 * QG * GG::NC, 4>();
-        if constexpr (MODE != kMass) settle(full_c, sA, pc_, 0, pb0, mx0, cs);
+        if constexpr (MODE != kMass) settle(full_c, std::true_type{}, sA, sB, pc_, bc, 0, pb0, mx0, cs);
 
         // R2: PV(half 0) || softmax(half 1)
-        pv_half(Vc, 0, pb0);
+        pv_half(Vc, mc, 0, pb0);
         if constexpr (MORE) cs_load<D, WAVES, ROT>(p, dnext, tid);
         softmax_half(full_c, sB, pc_, 1, pb1, mx1, cs);
         if constexpr (MODE != kMass) {
             interleave_hint<QG * (D / 16 + 1), 4>();
-            settle(full_c, sB, pc_, 1, pb1, mx1, cs);
+            settle(full_c, std::false_type{}, sB, sB, pc_, bc, 1, pb1, mx1, cs);
         }
 
         // R3: PV(half 1) || rotate + stage the next tile
-        pv_half(Vc, 1, pb1);
+        pv_half(Vc, mc, 1, pb1);
         if constexpr (MODE == kMass) {
             // Sum the 16 columns of the lane group: butterfly reduce-scatter,
             // afterwards lane lc holds the total of value index u = lc.
@@ -836,7 +911,8 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
         }
         if constexpr (MORE)
             data_store<D, WAVES, ROT>(dnext, Ks + (cur ^ 1) * GG::KBUF, Vs + (kV ? (cur ^ 1) * GG::VBUF : 0),
-                                      s_pi + (cur ^ 1) * kTileN, tid, kV, s_bias + (cur ^ 1) * kTileN);
+                                      s_pi + (cur ^ 1) * kTileN, tid, kV, s_bias + (cur ^ 1) * kTileN,
+                                      s_maskb + (cur ^ 1) * kTileN);
         if constexpr (MODE != kMass) interleave_hint<QG * (D / 16 + 1), 3>();
         __syncthreads();
 
@@ -912,7 +988,9 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     // ---- epilogue: per-lane partial sums -> column totals
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
-        const float lt = col_sum(acc_l[qg][0]);   // row 0 lives in lane group 0
+        // rows 0, 4, 8 and 12 (element 0 of the four lane groups) each hold
+        // the row sum: their total is exactly 4 times it
+        const float lt = col_sum(acc_l[qg][0]) * 0.25f;
         int t, h;
         if (!row_of(qg, t, h)) continue;
         const size_t rowid = (size_t)t * p.hq + h;
