@@ -153,6 +153,66 @@ def test_score_jumps_move_the_softmax_reference(op):
     say(f"  LSE: max {err.max():.3e}")
 
 
+def far_scores(q_len, decode=False):
+    """Every score a (query, head) row sees sits near one value per head, far
+    below or above zero, beside unusable slots with NaN / inf garbage inside
+    the tiles.  Queries and keys live in the lowest-frequency RoPE pair
+    (index 63 and 127 at d = 128), whose angle moves by about 2.4e-6 per
+    position at theta 5e5, so over these few hundred positions the rotation
+    is within 2e-3 of the identity and every score of a head is
+    -c m_h / sqrt(d) up to that.  In log2 units the heads of kv head 0 sit at
+    -20, -200, -8.5 and +30, those of kv head 1 at -10, -140, +2 and -40:
+    references far below zero, one past exp2's range, one just past the
+    slack, and positive ones."""
+    w = W.custom(119, Hq=8, Hkv=2, d=128, theta=5e5, span_lens=[[200, 150, 333]], gaps=[[0, 9, 2]],
+                 q_len=[q_len], decode=decode)
+    d = w.head_dim
+    log2e = np.log2(np.e)
+    c = 20.0 * np.sqrt(d) / log2e                     # m = 1 <-> -20 in log2 units
+    m = np.array([1.0, 10.0, 0.425, -1.5, 0.5, 7.0, -0.1, 2.0])
+    q = np.zeros((w.total_q, w.num_q_heads, d), np.float32)
+    q[:, :, 63] = m
+    w.q = W.f32_to_bf16_bits(q)
+    k = np.zeros(W.bf16_bits_to_f32(w.pool_k).shape, np.float32)
+    k[..., 63] = -c
+    w.pool_k = W.f32_to_bf16_bits(k)
+    # unusable slots inside the context, with garbage in K and V
+    rng = np.random.default_rng(9)
+    n = int(w.kv_len[0]) - (0 if decode else q_len)
+    holes = rng.choice(n, size=40, replace=False)
+    w.kv_pos[0, holes] = -1
+    for j, bits in ((holes[0], 0x7fc0), (holes[1], 0x7f80), (holes[2], 0xff80)):   # NaN, +inf, -inf
+        w.pool_k[w.block_table[0, j // 16], :, j % 16, :] = bits
+        w.pool_v[w.block_table[0, j // 16], :, :, j % 16] = bits
+    return w
+
+
+@pytest.mark.parametrize("case", ["prefill_160_rows", "prefill_20_rows", "decode"])
+def test_scores_far_from_zero_beside_unusable_keys(case):
+    """Bars: O as everywhere (the weights are near uniform, so the output is
+    near the mean of the visible values); LSE per row within the worst-case
+    effect of the bf16 rounding of the rotated q and k, as in the score-jump
+    test.  Counting an unusable key at the weight exp2(-reference) would move
+    the LSE by up to 200 log2 units, and an inf weight against a zero value
+    row would make O NaN."""
+    q_len = {"prefill_160_rows": 40, "prefill_20_rows": 5, "decode": 1}[case]
+    w = far_scores(q_len, decode=case == "decode")
+    ctx = H.ctx_for(w)
+    out, lse, _ = H.prefill(ctx, w) if case != "decode" else H.decode(ctx, w)
+    ref_o, ref_l = oracle.attention(w)
+    say(f"{case}: lse range {ref_l.min():.1f} .. {ref_l.max():.1f}")
+    o = H.host_bf16(out)
+    assert np.all(np.isfinite(o))
+    compare_out(o, ref_o, "O")
+    G = w.num_q_heads // w.num_kv_heads
+    qn = np.linalg.norm(W.bf16_bits_to_f32(w.q).astype(np.float64), axis=-1)             # [t][h]
+    kmax = 20.0 * np.sqrt(w.head_dim) / np.log2(np.e) * 1.01
+    err = np.abs(lse.cpu().numpy() - ref_l)
+    bound = 2.0 ** -8 * qn * kmax / np.sqrt(w.head_dim) + 2.0 ** -8
+    assert np.all(err <= bound), (float((err / bound).max()), np.unravel_index(np.argmax(err / bound), err.shape))
+    say(f"  LSE: max {err.max():.3e}, largest err / bound {(err / bound).max():.3f}")
+
+
 @pytest.mark.parametrize("name", ["shared_serving", "long_context"])
 def test_prefill_full_size_sampled(name):
     w = {"shared_serving": W.shared_serving, "long_context": W.long_context}[name]()
