@@ -448,9 +448,10 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(16))) float s_bias[2 * kTileN];
     // weight of each staged key in the row sums: bf16 1, or 0 if unusable
     __shared__ __attribute__((aligned(16))) uint16_t s_maskb[2 * kTileN];
-    // each lane's QK accumulator start per row tile, -u (4 equal values):
-    // read by the lane itself before every QK, rewritten when u moves
-    __shared__ __attribute__((aligned(16))) f32x4 s_negmu[MODE == kMass ? 1 : WAVES * QG * 64];
+    // the QK accumulator start of each query column per row tile, -u (4
+    // equal values): the 4 lanes of a column read it before every QK and
+    // rewrite it (the same value) when u moves
+    __shared__ __attribute__((aligned(16))) f32x4 s_negmu[MODE == kMass ? 1 : WAVES * QG * 16];
     __shared__ float s_red[MODE == kMass ? 2 * WAVES * kTileN : 1];
     __shared__ int32_t s_minpos, s_firstbad, s_lastbad, s_maxpos;
     // bit t: tile t holds a key that some row of the workgroup sees
@@ -665,12 +666,12 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
     // bias (-inf) before forming P.  thr: the check's threshold on the
     // half's lane max, the slack once set, else -FLT_MAX (any visible key).
     float m_ref[QG], thr[QG];
-    f32x4 *negmu = s_negmu + (MODE == kMass ? 0 : wave * QG * 64 + lane);   // row tile qg at [64 qg]
+    f32x4 *negmu = s_negmu + (MODE == kMass ? 0 : wave * QG * 16 + lc);   // row tile qg at [16 qg]
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
         m_ref[qg] = m_run[qg];
         thr[qg] = -FLT_MAX;
-        if constexpr (MODE != kMass) negmu[64 * qg] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (MODE != kMass) negmu[16 * qg] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     // ---- software pipeline over 32-key halves.  Per tile:
@@ -697,7 +698,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
             b1 = *reinterpret_cast<const f32x4 *>(bb + 4);
         } else {
 #pragma unroll
-            for (int qg = 0; qg < QG; ++qg) nm[qg] = negmu[64 * qg];
+            for (int qg = 0; qg < QG; ++qg) nm[qg] = negmu[16 * qg];
         }
         // d-chunk outermost: 2*QG independent accumulators separate the
         // dependent MFMAs of one accumulator chain
@@ -837,7 +838,7 @@ __global__ __launch_bounds__(64 * WAVES) void fwd_kernel(FwdParams p) {
                 const float delta = un - u;
                 m_ref[qg] = m_new;
                 thr[qg] = now ? kRescaleSlack : -FLT_MAX;
-                negmu[64 * qg] = f32x4{-un, -un, -un, -un};
+                negmu[16 * qg] = f32x4{-un, -un, -un, -un};
                 sacc[qg][0] -= delta;
                 sacc[qg][1] -= delta;
                 if constexpr (decltype(shift_other_c)::value) {
