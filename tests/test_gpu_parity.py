@@ -192,13 +192,14 @@ def test_scores_far_from_zero_beside_unusable_keys(case):
     """Bars: O as everywhere (the weights are near uniform, so the output is
     near the mean of the visible values); LSE per row within the worst-case
     effect of the bf16 rounding of the rotated q and k, as in the score-jump
-    test.  Counting an unusable key at the weight exp2(-reference) would move
+    test; the selection's mass and picks as in the selection tests, with and
+    without the caller's LSE.  Counting an unusable key at the weight exp2(-reference) would move
     the LSE by up to 200 log2 units, and an inf weight against a zero value
     row would make O NaN."""
     q_len = {"prefill_160_rows": 40, "prefill_20_rows": 5, "decode": 1}[case]
     w = far_scores(q_len, decode=case == "decode")
     ctx = H.ctx_for(w)
-    out, lse, _ = H.prefill(ctx, w) if case != "decode" else H.decode(ctx, w)
+    out, lse, dc = H.prefill(ctx, w) if case != "decode" else H.decode(ctx, w)
     ref_o, ref_l = oracle.attention(w)
     say(f"{case}: lse range {ref_l.min():.1f} .. {ref_l.max():.1f}")
     o = H.host_bf16(out)
@@ -211,6 +212,16 @@ def test_scores_far_from_zero_beside_unusable_keys(case):
     bound = 2.0 ** -8 * qn * kmax / np.sqrt(w.head_dim) + 2.0 ** -8
     assert np.all(err <= bound), (float((err / bound).max()), np.unravel_index(np.argmax(err / bound), err.shape))
     say(f"  LSE: max {err.max():.3e}, largest err / bound {(err / bound).max():.3f}")
+    if case == "decode":
+        return
+    # the selection over the same scores, with the caller's LSE and with its
+    # own K-only LSE pass (which shares the prefill's reference handling)
+    ref_m = oracle.mass(w)
+    ref_off, ref_idx = oracle.select(w, ref_m)
+    for lse_given in (True, False):
+        sel_off, sel, mass = H.select(ctx, w, dc, lse if lse_given else None)
+        check_selection(sel_off, sel, ref_off, ref_idx, ref_m, w)
+        check_mass(w, mass, ref_m, what=f"mass (caller's lse: {lse_given})")
 
 
 @pytest.mark.parametrize("name", ["shared_serving", "long_context"])
