@@ -709,6 +709,7 @@ def main():
                              kernel="fwd_kernel<128, 2, 8, 0, false, true>, step 1 (pic_attn_prefill's split "
                                     "partials; the merge kernel after it is not included)",
                              algorithmic_flops=flops, avg_ms=round(kern_ms["fwd_kernel step 1"], 5),
+                             qk_pairs_per_s=round(pairs * w.num_q_heads / (kern_ms["fwd_kernel step 1"] / 1e3), 1),
                              timing=f"HIP events stamped at the kernel's own start and end (the library launches "
                                     f"it with hipExtLaunchKernelGGL while timing is on), over {args.steps} "
                                     f"back-to-back step-1 prefill calls",
@@ -765,6 +766,7 @@ def main():
             "attended_kv_tokens_per_s": round(tl / (ml / 1e3), 1),
             "roofline": roof("mfma", fl / (kl / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
                              algorithmic_flops=fl, avg_ms=round(kl, 5), kernel="the prefill kernel",
+                             qk_pairs_per_s=round(pl * wl.num_q_heads / (kl / 1e3), 1),
                              note="near the MFMA/HBM ridge and launch-bound at one request"),
             "hbm": roof("hbm", kvb / (kl / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s", mp_hbm, algorithmic_bytes=kvb,
                         avg_ms=round(kl, 5))}
@@ -850,6 +852,7 @@ def main():
             "ms_per_call": round(ms_ss, 5), "attended_kv_tokens_per_s": round(tss / (ms_ss / 1e3), 1),
             "roofline": roof("mfma", fl / (k_ss / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
                              algorithmic_flops=fl, avg_ms=round(k_ss, 5), kernel="the prefill kernel",
+                             qk_pairs_per_s=round(pss * wss.num_q_heads / (k_ss / 1e3), 1),
                              call=roof("mfma", fl / (ms_ss / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
                                        avg_ms=round(ms_ss, 5), what="the whole pic_attn_prefill call"))}
         del dss, oss, lss, wsss
@@ -879,6 +882,7 @@ def main():
             "ms_per_call": round(rms, 5), "visible_pairs": pairs_r,
             "roofline": roof("mfma", flops_r / (krms / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
                              algorithmic_flops=flops_r, avg_ms=round(krms, 5),
+                             qk_pairs_per_s=round(pairs_r * w.num_q_heads / (krms / 1e3), 1),
                              kernel="fwd_kernel<128, 2, 8, 0, true, true> (tile skipping)",
                              call=roof("mfma", flops_r / (rms / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", mp_tf,
                                        avg_ms=round(rms, 5), what="the whole pic_attn_prefill call"))}
