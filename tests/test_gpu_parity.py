@@ -224,6 +224,51 @@ def test_scores_far_from_zero_beside_unusable_keys(case):
         check_mass(w, mass, ref_m, what=f"mass (caller's lse: {lse_given})")
 
 
+def out_of_range_values(decode):
+    """Device-side values outside their ranges, with max_position 4096: block
+    ids past the pool and negative, key positions at and past max_position, a
+    query at max_position - 1 (the table's last row) that sees a key there,
+    and a query at max_position.  Returns the workload the kernels get and the
+    one the oracle gets: the same, with those positions set to -1 (the
+    header's convention: such a key is unusable and such a row sees nothing;
+    the oracle already treats a block id outside the pool as unusable)."""
+    mp = 4096
+    w = W.custom(121, Hq=8, Hkv=2, d=128, theta=5e5, span_lens=[[200, 150], [300]], gaps=[[0, 11], [5]],
+                 q_len=[1, 1] if decode else [20, 5], decode=decode, max_position=mp)
+    nb = w.pool_k.shape[0]
+    w.block_table[0, 3] = nb + 5
+    w.block_table[0, 6] = -7
+    w.block_table[1, 2] = 2 ** 30
+    w.kv_pos[0, [20, 21, 150]] = [mp, mp + 100, 2 ** 30]
+    w.kv_pos[1, 40] = mp
+    # request 1: its first query moves to the table's last row and sees a key
+    # placed there; its last query (request 0's in decode) moves past the table
+    t1 = int(w.q_start[1])
+    w.q_pos[t1] = mp - 1
+    w.kv_pos[1, 77] = mp - 1
+    t_out = int(w.q_start[1]) - 1
+    w.q_pos[t_out] = mp
+    ref = dataclasses.replace(w, kv_pos=np.where(w.kv_pos >= mp, -1, w.kv_pos),
+                              q_pos=np.where(w.q_pos >= mp, -1, w.q_pos))
+    return w, ref, t_out
+
+
+@pytest.mark.parametrize("op", ["prefill", "decode"])
+def test_out_of_range_device_values(op):
+    """Bars as everywhere; the row whose query sits past the table sees
+    nothing (O = 0, LSE = -inf on both sides)."""
+    w, ref, t_out = out_of_range_values(op == "decode")
+    ctx = H.ctx_for(w)
+    out, lse, _ = H.prefill(ctx, w) if op == "prefill" else H.decode(ctx, w)
+    ref_o, ref_l = oracle.attention(ref)
+    o = H.host_bf16(out)
+    assert np.all(np.isfinite(o))
+    assert np.all(o[t_out] == 0) and np.all(np.isneginf(lse.cpu().numpy()[t_out]))
+    assert np.all(np.isneginf(ref_l[t_out]))
+    compare_out(o, ref_o, "O")
+    check_lse(ref, lse.cpu().numpy(), ref_l)
+
+
 @pytest.mark.parametrize("name", ["shared_serving", "long_context"])
 def test_prefill_full_size_sampled(name):
     w = {"shared_serving": W.shared_serving, "long_context": W.long_context}[name]()

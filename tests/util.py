@@ -35,9 +35,10 @@ SEL_BAND = 1e-3
 
 
 def lse_bar(w, rows=None) -> np.ndarray:
-    """Per-row LSE bar: the row's own error bar, capped at LSE_ABS."""
+    """Per-row LSE bar: the row's own error bar, capped at LSE_ABS (NaN, for a
+    row that sees nothing, stays NaN)."""
     from tests.error_model import bars
-    return np.fmin(bars(w, rows), LSE_ABS)
+    return np.minimum(bars(w, rows), LSE_ABS)
 
 
 def mass_bar(w, ref_mass) -> np.ndarray:
