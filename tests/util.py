@@ -179,10 +179,17 @@ def out_within(got, ref) -> bool:
     return mx <= O_MAX_ABS and mean <= O_MEAN_ABS and rel <= O_REL_L2
 
 
-def check_selection(gpu_off, gpu_idx, ref_off, ref_idx, ref_mass, w: Workload, band: float = SEL_BAND):
+def check_selection(gpu_off, gpu_idx, ref_off, ref_idx, ref_mass, w: Workload, band: float = None):
     """Selection contract: same CSR sizes; per span, every oracle-selected
     token outside the tie band is chosen and every oracle-rejected one outside
-    the band is not; the output is ascending and in the span."""
+    the band is not; the output is ascending and in the span.
+
+    band None (a mass selection): token j's band is the sum of its own mass
+    bar and the boundary token's (the bars check_mass holds each slot to),
+    at least SEL_BAND.  Two masses closer than that may come out in either
+    order within their bars.  A float: that band for every token (scores
+    with their own error bound, such as key norms)."""
+    bars = mass_bar(w, ref_mass) if band is None else None
     gpu_off = np.asarray(gpu_off)
     ref_off = np.asarray(ref_off)
     assert np.array_equal(gpu_off, ref_off), "per-span counts differ"
@@ -198,10 +205,12 @@ def check_selection(gpu_off, gpu_idx, ref_off, ref_idx, ref_mass, w: Workload, b
         assert g.min() >= st and g.max() < st + L
         assert np.all(w.kv_pos[r, g] >= 0)
         m = ref_mass[r]
-        boundary = np.min(m[o])
+        jb = int(o[np.argmin(m[o])])
+        boundary = m[jb]
         cand = [j for j in range(st, st + L) if j < w.kv_len[r] and w.kv_pos[r, j] >= 0]
         gs, os_ = set(g.tolist()), set(o.tolist())
         for j in cand:
-            if abs(m[j] - boundary) <= band:
+            tol = band if bars is None else max(SEL_BAND, float(bars[r, j] + bars[r, jb]))
+            if abs(m[j] - boundary) <= tol:
                 continue
             assert (j in gs) == (j in os_), f"span {s} token {j} mass {m[j]} boundary {boundary}"
