@@ -52,34 +52,38 @@ def random_layout(seed, decode=False):
 SHUFFLED_HEADS = [(8, 2), (4, 1), (16, 2), (8, 1)]
 
 
-def shuffled_layout(seed):
-    """One request of 2 to 5 spans of 64 to 599 tokens whose position ranges
-    are shuffled against their slot order (reused spans back at other
-    offsets), 64 to 160 query tokens (several row blocks at G = 8); in half the
-    seeds the queries sit at sorted random context positions (the sparse
-    recompute's queries), and in half about a tenth of the context slots are
-    masked."""
+def shuffled_layout(seed, decode=False):
+    """1 to 2 requests (seeds from 6 on) of 2 to 5 spans of 64 to 599 tokens
+    whose position ranges are shuffled against their slot order (reused spans
+    back at other offsets), 64 to 160 query tokens (several row blocks at
+    G = 8) or one in decode; in half the prefill seeds the queries sit at
+    sorted random context positions (the sparse recompute's queries), and in
+    half about a tenth of the context slots are masked."""
     rng = np.random.default_rng(seed)
     hq, hkv = SHUFFLED_HEADS[int(rng.integers(len(SHUFFLED_HEADS)))]
     d = int(rng.choice([64, 128]))
-    lens = [int(x) for x in rng.integers(64, 600, size=int(rng.integers(2, 6)))]
-    nq = int(rng.integers(64, 161))
-    w = W.custom(3000 + seed, Hq=hq, Hkv=hkv, d=d, theta=float(rng.choice([1e4, 5e5])), span_lens=[lens],
-                 q_len=[nq], ratio=float(rng.choice([0.1, 0.25, 0.5])))
-    base, pos = {}, 0
-    for s in rng.permutation(len(lens)):
-        base[int(s)] = pos
-        pos += lens[s]
-    for s in range(len(lens)):
-        st = int(w.span_start[s])
-        assert int(w.span_len[s]) == lens[s]
-        w.kv_pos[0, st:st + lens[s]] = base[s] + np.arange(lens[s])
-    n_ctx = int(w.kv_len[0]) - nq
-    if rng.random() < 0.5:
-        ctx_pos = w.kv_pos[0, :n_ctx]
-        w.q_pos[:] = np.sort(rng.choice(ctx_pos[ctx_pos >= 0], size=nq, replace=False))
-    if rng.random() < 0.5:
-        w.kv_pos[0, rng.choice(n_ctx, size=n_ctx // 10, replace=False)] = -1
+    batch = 1 if seed < 6 else 2
+    lens = [[int(x) for x in rng.integers(64, 600, size=int(rng.integers(2, 6)))] for _ in range(batch)]
+    nq = [1 if decode else int(rng.integers(64, 161)) for _ in range(batch)]
+    w = W.custom(3000 + seed, Hq=hq, Hkv=hkv, d=d, theta=float(rng.choice([1e4, 5e5])), span_lens=lens,
+                 q_len=nq, ratio=float(rng.choice([0.1, 0.25, 0.5])), decode=decode)
+    for r in range(batch):
+        spans = [s for s in range(len(w.span_req)) if int(w.span_req[s]) == r]
+        assert [int(w.span_len[s]) for s in spans] == lens[r]
+        base, pos = {}, 0
+        for s in rng.permutation(spans):
+            base[int(s)] = pos
+            pos += int(w.span_len[s])
+        for s in spans:
+            st, L = int(w.span_start[s]), int(w.span_len[s])
+            w.kv_pos[r, st:st + L] = base[s] + np.arange(L)
+        n_ctx = int(w.kv_len[r]) - (0 if decode else nq[r])
+        if not decode and rng.random() < 0.5:
+            ctx_pos = w.kv_pos[r, :n_ctx]
+            q0 = int(w.q_start[r])
+            w.q_pos[q0:q0 + nq[r]] = np.sort(rng.choice(ctx_pos[ctx_pos >= 0], size=nq[r], replace=False))
+        if rng.random() < 0.5:
+            w.kv_pos[r, rng.choice(n_ctx, size=n_ctx // 10, replace=False)] = -1
     return w
 
 
@@ -94,7 +98,7 @@ def check_out(got, ref, what):
     assert out_within(got, ref), (what, mx, mean, rel)
 
 
-@pytest.mark.parametrize("seed", list(range(10)) + [f"shuffled{i}" for i in range(6)])
+@pytest.mark.parametrize("seed", list(range(10)) + [f"shuffled{i}" for i in range(10)])
 def test_random_layout_prefill_select_fuse(seed):
     w = shuffled_layout(int(seed[8:])) if isinstance(seed, str) else random_layout(seed)
     say(f"seed {seed}: {describe(w)}")
@@ -129,9 +133,9 @@ def test_random_layout_prefill_select_fuse(seed):
     check_lse(fused, lse2.cpu().numpy(), refl2)
 
 
-@pytest.mark.parametrize("seed", range(10, 16))
+@pytest.mark.parametrize("seed", list(range(10, 16)) + [f"shuffled{i}" for i in range(20, 26)])
 def test_random_layout_decode(seed):
-    w = random_layout(seed, decode=True)
+    w = shuffled_layout(int(seed[8:]), decode=True) if isinstance(seed, str) else random_layout(seed, decode=True)
     say(f"seed {seed}: {describe(w)}")
     ctx = H.ctx_for(w)
     out, lse, _ = H.decode(ctx, w)
