@@ -291,6 +291,39 @@ def test_prefill_full_size_sampled(name):
     assert np.all(np.isfinite(H.host_bf16(out)))
 
 
+def test_longest_context_prefill_select_decode():
+    """The largest context the default RoPE table holds: 63 reused 1024-token
+    spans + 256 query tokens = 64,768 slots, positions up to 64,767 of 65,536.
+    Prefill on sampled rows against the oracle, the selection's size-independent
+    properties, and a one-token decode over the same spans against the oracle."""
+    w = W.long_context(n_spans=63)
+    assert w.max_kv_len == 64768 and int(w.q_pos.max()) < w.max_position
+    say(f"longest context: kv={w.max_kv_len} q={w.max_q_len} max pos {int(w.q_pos.max())}")
+    ctx = H.ctx_for(w)
+    out, lse, dc = H.prefill(ctx, w)
+    rng = np.random.default_rng(11)
+    ts = np.concatenate([[0, w.total_q - 1], rng.integers(0, w.total_q, 14)])
+    hs = rng.integers(0, w.num_q_heads, len(ts))
+    ref_o, ref_l = oracle.attention(w, (ts, hs))
+    compare_out(H.host_bf16(out)[ts, hs], ref_o, "O sampled")
+    check_lse(w, lse.cpu().numpy()[ts, hs], ref_l, rows=(ts, hs))
+    sel_off, sel, mass = H.select(ctx, w, dc, lse)
+    n = int(w.kv_len[0])
+    total = float(mass[0, :n].astype(np.float64).sum())
+    say(f"  mass sum {total:.3f} expected {w.total_q * w.num_q_heads}")
+    assert abs(total - w.total_q * w.num_q_heads) <= 1e-4 * w.total_q * w.num_q_heads
+    for s in range(len(w.span_req)):
+        st, L = int(w.span_start[s]), int(w.span_len[s])
+        k = int(sel_off[s + 1] - sel_off[s])
+        order = sorted(range(st, st + L), key=lambda j: (-float(mass[0, j]), j))
+        assert list(sel[sel_off[s]:sel_off[s + 1]]) == sorted(order[:k])
+    wd = W.long_context(n_spans=63, q_len=1)
+    dout, dlse, _ = H.decode(ctx, wd)
+    ref_o, ref_l = oracle.attention(wd)
+    compare_out(H.host_bf16(dout), ref_o, "decode O")
+    check_lse(wd, dlse.cpu().numpy(), ref_l)
+
+
 # ---------------------------------------------------------------- decode
 
 @pytest.mark.parametrize("name", ["small", "small_private", "edge_g8", "masked_garbage", "d64", "d64_irregular"])
