@@ -436,8 +436,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--clock-warmup-s", type=float, default=1.0,
                     help="seconds of eager steps before any timing (the clock settles under load)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=16)
-    ap.add_argument("--cpu-all-tokens", type=int, default=64)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32)
+    ap.add_argument("--cpu-all-tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--only", default=",".join(LINES),
