@@ -97,6 +97,22 @@ FwdPlan plan_fwd(const pic_config &c, int batch, int max_q_len, int max_kv_len) 
     return pl;
 }
 
+// The selection's own LSE pass (lse == NULL): it keeps no O accumulator, so
+// at d = 128 a request with more than 256 rows per kv head takes 4 row tiles
+// per wave (shape 4, 512-row workgroups) unless it has the many row blocks of
+// the tile-skipping variant.  Up to 256 rows a 512-row workgroup would leave
+// half its waves on rows that do not exist.
+FwdPlan plan_lse(const pic_config &c, int batch, int max_q_len, int max_kv_len) {
+    FwdPlan pl = plan_fwd(c, batch, max_q_len, max_kv_len);
+    const long long rows = (long long)max_q_len * (c.num_q_heads / c.num_kv_heads);
+    if (pl.shape != 1 || c.head_dim != 128 || rows <= 256) return pl;
+    pl.shape = 4;
+    pl.rows_per_block = pic::fwd_rows_per_block(c.head_dim, 4);
+    pl.row_blocks = (int)((rows + pl.rows_per_block - 1) / pl.rows_per_block);
+    set_splits(pl, c, batch, max_kv_len);
+    return pl;
+}
+
 // The selection mass pass: at shape >= 1 its workgroups hold twice the rows
 // (4 row tiles per wave: it keeps no O accumulator), and it never skips
 // tiles.  At d = 128 a request of at most 256 rows per kv head takes 2 row
@@ -430,7 +446,7 @@ pic_status pic_workspace_bytes(const pic_ctx *ctx, pic_op op, const pic_req_tabl
         return PIC_OK;
     case PIC_OP_SELECT: {
         if (total_q < 0 || max_q_len < 0) return PIC_ERR_INVALID_ARG;
-        const FwdPlan pl = plan_fwd(c, req->batch, max_q_len, req->max_kv_len);
+        const FwdPlan pl = plan_lse(c, req->batch, max_q_len, req->max_kv_len);
         const FwdPlan plm = plan_mass(c, req->batch, max_q_len, req->max_kv_len);
         *bytes = select_ws(c, pl, plm, req->batch, req->max_blocks, total_q, req->max_kv_len).total;
         return PIC_OK;
@@ -566,7 +582,7 @@ pic_status qc_score_select(pic_ctx *ctx, const pic_kv_pool *pool, const pic_req_
     if (max_sel < 0 || (max_sel > 0 && !sel_idx)) return fail(ctx, PIC_ERR_INVALID_ARG, "sel_idx / max_sel invalid%s");
     if (req->batch == 0) return PIC_OK;
     const pic_config &c = ctx->cfg;
-    const FwdPlan pl = plan_fwd(c, req->batch, qs->max_q_len, req->max_kv_len);
+    const FwdPlan pl = plan_lse(c, req->batch, qs->max_q_len, req->max_kv_len);
     const FwdPlan plm = plan_mass(c, req->batch, qs->max_q_len, req->max_kv_len);
     const SelectWs w = select_ws(c, pl, plm, req->batch, req->max_blocks, qs->total_q, req->max_kv_len);
     if (!ws || ws_bytes < w.total) return fail(ctx, PIC_ERR_WORKSPACE, "workspace too small for selection%s");
@@ -645,7 +661,7 @@ pic_status qc_score_select_noalloc(pic_ctx *ctx, const pic_kv_pool *pool, const 
     if (st != PIC_OK) return st;
     if ((st = check_queries(ctx, qs, req->batch)) != PIC_OK) return st;
     const pic_config &c = ctx->cfg;
-    const FwdPlan pl = plan_fwd(c, req->batch, qs->max_q_len, req->max_kv_len);
+    const FwdPlan pl = plan_lse(c, req->batch, qs->max_q_len, req->max_kv_len);
     const FwdPlan plm = plan_mass(c, req->batch, qs->max_q_len, req->max_kv_len);
     const size_t need = select_ws(c, pl, plm, req->batch, req->max_blocks, qs->total_q, req->max_kv_len).total;
     if (need > (size_t)PIC_NOALLOC_SCRATCH_BYTES) {

@@ -1433,10 +1433,17 @@ hipError_t launch_shape(const FwdParams &p, int shape, hipStream_t s, const Kern
         }
         return launch_one<D, 4, D == 128 ? 8 : 4, MODE, false>(p, s, ev);
     }
-    else if constexpr (D == 128)
-        return shape == 2 ? launch_one<D, 2, 8, MODE, S>(p, s, ev) : launch_one<D, 2, 8, MODE, false>(p, s, ev);
-    else
-        return shape == 2 ? launch_one<D, 2, 4, MODE, S>(p, s, ev) : launch_one<D, 2, 4, MODE, false>(p, s, ev);
+    else {
+        // the LSE pass keeps no O accumulator: 4 row tiles per wave (shape 4,
+        // d = 128)
+        if constexpr (MODE == kLse && D == 128) {
+            if (shape == 4) return launch_one<D, 4, 8, MODE, false>(p, s, ev);
+        }
+        if constexpr (D == 128)
+            return shape == 2 ? launch_one<D, 2, 8, MODE, S>(p, s, ev) : launch_one<D, 2, 8, MODE, false>(p, s, ev);
+        else
+            return shape == 2 ? launch_one<D, 2, 4, MODE, S>(p, s, ev) : launch_one<D, 2, 4, MODE, false>(p, s, ev);
+    }
 }
 
 template <int D>
@@ -1450,7 +1457,10 @@ hipError_t launch_mode(const FwdParams &p, int mode, int shape, hipStream_t s, c
 
 }  // namespace
 
-int fwd_rows_per_block(int head_dim, int shape) { return shape == 0 ? 64 : (head_dim == 128 ? 256 : 128); }   // 2 as 1
+int fwd_rows_per_block(int head_dim, int shape) {
+    if (shape == 4) return 512;   // the LSE pass with 4 row tiles per wave (d = 128)
+    return shape == 0 ? 64 : (head_dim == 128 ? 256 : 128);   // 2 as 1
+}
 int mass_rows_per_block(int head_dim, int shape) {
     return head_dim == 128 ? (shape == 3 ? 256 : 512) : 256;
 }

@@ -142,7 +142,8 @@ struct KernelEvents {
 
 // Launchers (return the launch's hipError_t).
 // shape 0: 64 rows per workgroup; shape 1: 256 rows (d = 128) / 128 rows (d = 64);
-// shape 2: shape 1 skipping the tiles that no row of a workgroup sees
+// shape 2: shape 1 skipping the tiles that no row of a workgroup sees; shape 4
+// (LSE mode at d = 128 only): 4 row tiles per wave, 512 rows
 int fwd_rows_per_block(int head_dim, int shape);
 // rows per workgroup of the mass pass at shape >= 1: 4 row tiles per wave, or
 // 2 at shape 3 (d = 128 only)

@@ -187,7 +187,7 @@ def far_scores(q_len, decode=False):
     return w
 
 
-@pytest.mark.parametrize("case", ["prefill_160_rows", "prefill_20_rows", "decode"])
+@pytest.mark.parametrize("case", ["prefill_320_rows", "prefill_160_rows", "prefill_20_rows", "decode"])
 def test_scores_far_from_zero_beside_unusable_keys(case):
     """Bars: O as everywhere (the weights are near uniform, so the output is
     near the mean of the visible values); LSE per row within the worst-case
@@ -196,7 +196,9 @@ def test_scores_far_from_zero_beside_unusable_keys(case):
     without the caller's LSE.  Counting an unusable key at the weight exp2(-reference) would move
     the LSE by up to 200 log2 units, and an inf weight against a zero value
     row would make O NaN."""
-    q_len = {"prefill_160_rows": 40, "prefill_20_rows": 5, "decode": 1}[case]
+    # 320 rows per kv head: two 256-row blocks of the prefill, one 512-row
+    # block of the selection's own LSE pass
+    q_len = {"prefill_320_rows": 80, "prefill_160_rows": 40, "prefill_20_rows": 5, "decode": 1}[case]
     w = far_scores(q_len, decode=case == "decode")
     ctx = H.ctx_for(w)
     out, lse, dc = H.prefill(ctx, w) if case != "decode" else H.decode(ctx, w)
