@@ -312,10 +312,13 @@ __global__ void fuse_len_kernel(FuseParams p) {
 // Anchor score of every slot of a request (QCFuse, gist.science 2604.08585,
 // methodology A / phase 1: anchors are the tokens with the highest key norms):
 // the squared norm of the stored (unrotated) key over all kv heads, 0 for
-// unusable slots.  One workgroup per 16-slot block, each wave 4 slots; a lane
-// sums the squares of its 16-byte chunks of the slot's key (bf16 squares are
-// exact in fp32) and a fixed-order butterfly adds the lanes: deterministic.
-// HBM-bound: every usable key is read once.
+// unusable slots.  One workgroup per 16-slot block, each 16-lane group one
+// slot; a lane sums the squares of its 16-byte chunks of the slot's key (bf16
+// squares are exact in fp32), chunks i, i + 16, ... in that order, and a
+// fixed-order butterfly adds the 16 lanes: deterministic.  The block id comes
+// first; every chunk of a lane is then requested before the first add, so a
+// workgroup waits on two memory round trips.  HBM-bound: every usable key is
+// read once.
 template <int D>
 __global__ __launch_bounds__(256) void key_norm_kernel(NormParams p) {
     const int b = blockIdx.x, r = blockIdx.y;
@@ -325,33 +328,39 @@ __global__ __launch_bounds__(256) void key_norm_kernel(NormParams p) {
     if (b * kBlock >= kvl) return;
     const int blk = p.block_table[(size_t)r * p.max_blocks + b];
     const bool bok = (unsigned)blk < (unsigned)p.num_blocks;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 15;
+    const int off = threadIdx.x >> 4, j = b * kBlock + off;   // slot of this lane's group
+    const int pi = p.kv_pos[(size_t)r * kv_stride + j];       // j < kv_stride: b < max_blocks
     constexpr int CPR = D / 8;               // 16-byte chunks per head row
+    constexpr int BATCH = 8;                 // chunks of a lane requested together
     const int nch = p.hkv * CPR;             // chunks of one slot's key
+    float acc = 0.f;
+    if (bok) {
+        for (int c0 = lane; c0 < nch; c0 += 16 * BATCH) {
+            u32x4 v[BATCH];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int off = 4 * wave + u, j = b * kBlock + off;
-        if (j >= kvl) break;                 // wave-uniform
-        const int pi = p.kv_pos[(size_t)r * kv_stride + j];
-        const bool ok = bok && (unsigned)pi < (unsigned)p.max_pos;
-        float acc = 0.f;
-        if (ok) {
-            for (int c = lane; c < nch; c += 64) {
-                const int g = c / CPR, cc = c % CPR;
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(
+            for (int u = 0; u < BATCH; ++u) {
+                const int c = c0 + 16 * u;
+                const int cl = c < nch ? c : 0;   // a chunk of the key: every load stays in the row
+                const int g = cl / CPR, cc = cl % CPR;
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(
                     p.k_pool + (((size_t)blk * p.hkv + g) * kBlock + off) * D + 8 * cc);
+                v[u] = c < nch ? x : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float lo = __uint_as_float(v[e] << 16), hi = __uint_as_float(v[e] & 0xffff0000u);
+                    const float lo = __uint_as_float(v[u][e] << 16), hi = __uint_as_float(v[u][e] & 0xffff0000u);
                     acc = fmaf(lo, lo, acc);
                     acc = fmaf(hi, hi, acc);
                 }
-            }
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-        if (lane == 0) p.norm[(size_t)r * kv_stride + j] = ok ? acc : 0.f;
     }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    const bool ok = bok && (unsigned)pi < (unsigned)p.max_pos;
+    if (lane == 0 && j < kvl) p.norm[(size_t)r * kv_stride + j] = ok ? acc : 0.f;
 }
 
 }  // namespace
