@@ -49,63 +49,29 @@ __global__ __launch_bounds__(256) void mass_reduce_kernel(SelectParams p) {
     p.mass[(size_t)r * p.kv_stride + j] = s;
 }
 
-// Exclusive prefix count of `flag` over the 256 threads, in thread order.
-// Returns the prefix; *total gets the workgroup total.  Uses s_cnt[4].
-__device__ __forceinline__ int block_excl_count(bool flag, int *s_cnt, int *total) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const unsigned long long m = __ballot(flag);
-    const int below = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) s_cnt[wave] = __popcll(m);
-    __syncthreads();
-    int pre = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const int c = s_cnt[w];
-        pre += w < wave ? c : 0;
-        tot += c;
-    }
-    __syncthreads();
-    *total = tot;
-    return pre + below;
-}
-
 constexpr int kTopkCache = 8;   // keys per thread kept in registers: spans up to 2048 slots
-
-// Inclusive prefix sum over the 256 threads in thread order (uses s_w[4]).
-__device__ __forceinline__ int block_incl_sum(int x, int *s_w) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) s_w[wave] = x;
-    __syncthreads();
-    int add = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) add += w < wave ? s_w[w] : 0;
-    __syncthreads();
-    return x + add;
-}
 
 // Per-span top-k of the mass (QCFuse selection): a 4 x 8-bit radix select
 // finds the k-th largest key (masses are >= 0, so their float bits order
 // like the values), then one in-order pass keeps the keys above it and the
 // first of the keys equal to it (ties go to the lower slot index).  Spans of
-// up to 2048 slots keep their keys in registers; the digit of each pass is
-// found by a parallel suffix scan of the 256-bin histogram.
+// up to 2048 slots keep their keys in registers.  Barriers: two per radix
+// pass (the histograms are double-buffered and every wave scans all 256 bins
+// itself, so no digit is broadcast) and one per 256-key chunk of the output
+// pass (each wave publishes its counts of larger and of equal keys, from
+// which every thread places its own).
 __global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
-    __shared__ int s_hist[256];
-    __shared__ int s_cnt[4];
-    __shared__ int s_w[4];
-    __shared__ uint32_t s_sel[2];
+    __shared__ __attribute__((aligned(16))) int s_hist[2][256];
+    __shared__ int s_cnt[2][kWaves][2];   // per chunk parity and wave: keys larger than, equal to the threshold
     const int s = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int r = p.span_req[s], st = p.span_start[s], L = p.span_len[s];
     const int k = p.sel_off[s + 1] - p.sel_off[s];
     int32_t *out = p.sel_idx + p.sel_off[s];
     if (r < 0 || r >= p.batch || k <= 0) return;
     const int32_t *pis = p.kv_pos + (size_t)r * p.kv_stride;
     const float *mass = p.mass + (size_t)r * p.kv_stride;
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;   // the lanes under this one
     // A span that fits in registers requests its slots (clamped into the
     // request's row) beside the request's length, not after it.
     const int lo = max(st, 0), hi_span = min(st + max(L, 0), p.kv_stride);
@@ -126,23 +92,23 @@ __global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
 
     uint32_t ck[kTopkCache];
     bool cc[kTopkCache];
-    // visit(j, key, is_candidate) over this thread's slots, in chunk order
+    // visit(j, key, is_candidate) over this thread's slots, in chunk order;
+    // every thread visits the same number of chunks
     auto visit = [&](auto &&f) {
         if (cached) {
 #pragma unroll
             for (int u = 0; u < kTopkCache; ++u) {
                 if (lo + 256 * u >= hi) break;
-                f(u, lo + 256 * u + tid, ck[u], cc[u]);
+                f(lo + 256 * u + tid, ck[u], cc[u]);
             }
         } else {
-            for (int u = 0, base = lo; base < hi; ++u, base += 256) {
+            for (int base = lo; base < hi; base += 256) {
                 const int j = base + tid;
                 const bool c = j < hi && pis[j] >= 0;
-                f(u, j, c ? __float_as_uint(mass[j]) : 0u, c);
+                f(j, c ? __float_as_uint(mass[j]) : 0u, c);
             }
         }
     };
-    int mine = 0;
     if (cached) {
 #pragma unroll
         for (int u = 0; u < kTopkCache; ++u) {
@@ -150,64 +116,101 @@ __global__ __launch_bounds__(256) void span_topk_kernel(SelectParams p) {
             const bool c = j < hi && cpi[u] >= 0;
             cc[u] = c;
             ck[u] = c ? cms[u] : 0u;
-            mine += c;
         }
-    } else {
-        visit([&](int, int, uint32_t, bool c) { mine += c; });
     }
-    s_cnt[0] = 0;
+    s_hist[0][tid] = 0;
+    s_hist[1][tid] = 0;
     __syncthreads();
-    if (mine) atomicAdd(&s_cnt[0], mine);
-    __syncthreads();
-    const int total = s_cnt[0];
-    __syncthreads();
-    const int kk = min(k, total);
-    uint32_t thr = 0;
-    int take_eq = 0;
-    const bool take_all = kk == total;
-    if (!take_all) {
-        uint32_t prefix = 0, pmask = 0;
-        int rem = kk;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            s_hist[tid] = 0;
-            __syncthreads();
-            visit([&](int, int, uint32_t key, bool c) {
-                if (c && (key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255], 1);
-            });
-            __syncthreads();
-            // thread t covers digit 255 - t: x = number of keys with that digit
-            // or a larger one; the selected digit is the one where x first
-            // reaches rem
-            const int h = s_hist[255 - tid];
-            const int x = block_incl_sum(h, s_w);
-            const int before = x - h;
-            if (before < rem && x >= rem) {
-                s_sel[0] = (uint32_t)(255 - tid);
-                s_sel[1] = (uint32_t)(rem - before);
-            }
-            __syncthreads();
-            prefix |= s_sel[0] << shift;
-            pmask |= 255u << shift;
-            rem = (int)s_sel[1];
-            __syncthreads();
+
+    // Radix passes.  The first one histograms every candidate, so its bins
+    // also give their number.
+    uint32_t prefix = 0, pmask = 0, thr = 0;
+    int rem = 0, kk = 0, take_eq = 0;
+    bool take_all = false;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        int *h = s_hist[pass & 1];
+        visit([&](int, uint32_t key, bool c) {
+            if (c && (key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255], 1);
+        });
+        __syncthreads();   // the histogram is complete
+        // lane l of every wave: digits 255-4l .. 252-4l, counted from the top
+        const int4 hv = *reinterpret_cast<const int4 *>(h + 252 - 4 * lane);
+        // the other buffer, last read in the previous pass, is the next one's
+        s_hist[(pass + 1) & 1][tid] = 0;
+        const int t = hv.x + hv.y + hv.z + hv.w;
+        int incl = t;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
         }
+        if (pass == 0) {
+            const int total = __shfl(incl, 63);
+            kk = min(k, total);
+            take_all = kk == total;   // the same in every wave
+            rem = kk;
+            if (take_all) break;
+        }
+        const int excl = incl - t;
+        const int c3 = excl + hv.w, c2 = c3 + hv.z, c1 = c2 + hv.y;
+        // the digit where the count from the top first reaches rem, and the
+        // count of keys with a larger digit
+        int dig, above;
+        if (c3 >= rem) {
+            dig = 255 - 4 * lane;
+            above = excl;
+        } else if (c2 >= rem) {
+            dig = 254 - 4 * lane;
+            above = c3;
+        } else if (c1 >= rem) {
+            dig = 253 - 4 * lane;
+            above = c2;
+        } else {
+            dig = 252 - 4 * lane;
+            above = c1;
+        }
+        const uint64_t m = __ballot(excl < rem && incl >= rem);
+        const int src = m ? (int)__builtin_ctzll(m) : 63;
+        prefix |= (uint32_t)__shfl(dig, src) << shift;
+        pmask |= 255u << shift;
+        rem -= __shfl(above, src);
+        __syncthreads();   // the next histogram is cleared before its atomics
+    }
+    if (!take_all) {
         thr = prefix;
         take_eq = rem;
     }
     // in-order pass: larger than the threshold, or equal and among the first
     // take_eq equal ones (lowest indices)
-    int out_base = 0, eq_base = 0;
-    visit([&](int, int j, uint32_t key, bool cand) {
+    int out_base = 0, eq_base = 0, chunk = 0;
+    visit([&](int j, uint32_t key, bool cand) {
         const bool gt = cand && (take_all || key > thr);
         const bool eq = cand && !take_all && key == thr;
-        int eq_tot;
-        const int eq_rank = block_excl_count(eq, s_cnt, &eq_tot);
-        const bool take = gt || (eq && eq_base + eq_rank < take_eq);
-        int take_tot;
-        const int pos = block_excl_count(take, s_cnt, &take_tot);
-        if (take && p.sel_off[s] + out_base + pos < p.max_sel) out[out_base + pos] = j;
-        out_base += take_tot;
+        const uint64_t gm = __ballot(gt), em = __ballot(eq);
+        int(*cnt)[2] = s_cnt[chunk & 1];
+        if (lane == 0) {
+            cnt[wave][0] = __popcll(gm);
+            cnt[wave][1] = __popcll(em);
+        }
+        __syncthreads();
+        int gt_lo = 0, eq_lo = 0, gt_tot = 0, eq_tot = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int g = cnt[w][0], e = cnt[w][1];
+            gt_lo += w < wave ? g : 0;
+            eq_lo += w < wave ? e : 0;
+            gt_tot += g;
+            eq_tot += e;
+        }
+        const int eq_room = max(take_eq - eq_base, 0);   // equal keys still to take, in index order
+        const bool take = gt || (eq && eq_lo + __popcll(em & below) < eq_room);
+        const uint64_t tm = __ballot(take);
+        const int pos = out_base + gt_lo + min(eq_lo, eq_room) + __popcll(tm & below);
+        if (take && p.sel_off[s] + pos < p.max_sel) out[pos] = j;
+        out_base += gt_tot + min(eq_tot, eq_room);
         eq_base += eq_tot;
+        ++chunk;
     });
     for (int i = kk + tid; i < k; i += 256)
         if (p.sel_off[s] + i < p.max_sel) out[i] = -1;
