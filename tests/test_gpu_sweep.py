@@ -3,7 +3,8 @@
 Each seed draws a head layout (G = 1 .. 8), d (64 or 128), 1 to 3 requests of
 1 to 3 spans (lengths 1 .. 399, gaps 0 .. 49 positions), 1 .. 47 query tokens
 and a selection ratio, and masks about a tenth of some requests' context
-slots (pi = -1).  Every seed runs prefill with LSE, the selection, the fusion
+slots (pi = -1).  Every seed runs prefill with LSE, the selection (with that
+LSE and with its own LSE pass), the fusion
 of the oracle's own selection and attention over the fused cache; a second
 set runs decode (one query token per request).  Bars as in
 test_gpu_parity.py.
@@ -108,11 +109,14 @@ def test_random_layout_prefill_select_fuse(seed):
     check_out(H.host_bf16(out), ref_o, "O")
     check_lse(w, lse.cpu().numpy(), ref_l)
 
-    sel_off, sel, mass = H.select(ctx, w, dc, lse)
     ref_m = oracle.mass(w)
     ref_off, ref_idx = oracle.select(w, ref_m)
-    check_selection(sel_off, sel, ref_off, ref_idx, ref_m, w)
-    check_mass(w, mass, ref_m)
+    # with the prefill's LSE, and with the selection's own K-only LSE pass
+    # (512-row workgroups above 256 rows per kv head at d = 128)
+    for lse_in in (lse, None):
+        sel_off, sel, mass = H.select(ctx, w, dc, lse_in)
+        check_selection(sel_off, sel, ref_off, ref_idx, ref_m, w)
+        check_mass(w, mass, ref_m, what=f"mass (caller's lse: {lse_in is not None})")
 
     # fuse the oracle's own selection on both sides, then attend again
     req_off = H.req_offsets(w, ref_off)
